@@ -1,0 +1,538 @@
+// Host runtime of libpd_attn.so: argument checks, the planner, the device
+// workspace image, and the C entry points declared in include/pd_attn.h.
+//
+// The planner splits one step of a ragged batch (Perplexity, "Disaggregated
+// prefill and decode", section "Prefill vs Decode performance": prefill and
+// decode requests batched together, attention parallel over requests and
+// kv_len) into
+//   * prefill tiles: up to 128 query rows (tokens x the g query heads of one
+//     KV head) over the tile's causal key range, one 256-thread block each,
+//     ordered so that the tiles of one (request, KV head) share an XCD and
+//     longest tiles start first;
+//   * decode units: the <= 16 query rows of one (request, KV head) over a
+//     chunk of keys, one wavefront each, the request's kv_len cut into equal
+//     chunks so that the units keep every CU busy;
+//   * merge groups: the chunks of one (request, KV head).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "pd_attn.h"
+#include "pd_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pd_status fail(pd_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dispatched round robin
+
+pd_status check_desc(const pd_attn_desc* d) {
+  if (!d) return fail(PD_ERR_INVALID_ARG, "desc is NULL");
+  if (d->num_qo_heads < 1 || d->num_kv_heads < 1)
+    return fail(PD_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (d->num_qo_heads % d->num_kv_heads != 0)
+    return fail(PD_ERR_INVALID_ARG, "num_qo_heads must be a multiple of num_kv_heads");
+  if (d->num_qo_heads / d->num_kv_heads > pdk::kPrefillRows)
+    return fail(PD_ERR_UNSUPPORTED, "query heads per KV head must be <= 128");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PD_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (d->page_size != 16 && d->page_size != 32 && d->page_size != 64 && d->page_size != 128)
+    return fail(PD_ERR_UNSUPPORTED, "page_size must be 16, 32, 64 or 128");
+  if (d->dtype != PD_F32 && d->dtype != PD_BF16)
+    return fail(PD_ERR_UNSUPPORTED, "dtype must be PD_F32 or PD_BF16");
+  if (d->causal != 0 && d->causal != 1) return fail(PD_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!std::isfinite(d->sm_scale)) return fail(PD_ERR_INVALID_ARG, "sm_scale must be finite");
+  return PD_OK;
+}
+
+int elt_bytes(const pd_attn_desc* d) { return d->dtype == PD_F32 ? 4 : 2; }
+
+int64_t page_bytes_of(const pd_attn_desc* d) {
+  return 2LL * d->num_kv_heads * d->page_size * d->head_dim * elt_bytes(d);
+}
+
+}  // namespace
+
+struct pd_plan_s {
+  pd_attn_desc desc{};
+  int32_t B = 0, g = 1, total_rows = 0, chunk_keys = 0, n_parts = 0;
+  std::vector<int32_t> qo_indptr;
+  std::vector<pdk::ReqInfo> req;
+  std::vector<int32_t> pages;
+  std::vector<pdk::PrefillItem> pf;
+  std::vector<pdk::DecodeItem> du;
+  std::vector<pdk::MergeGroup> mg;
+  size_t off_qo = 0, off_req = 0, off_pages = 0, off_pf = 0, off_du = 0, off_mg = 0;
+  size_t meta_bytes = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
+  int64_t prefill_flops = 0, decode_bytes = 0;
+  std::vector<char> blob;  // host image of the workspace tables
+  void* pinned = nullptr;
+  hipEvent_t ev = nullptr;
+  bool ev_recorded = false;
+};
+
+namespace {
+
+pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
+  const pd_attn_desc& d = P.desc;
+  const int g = P.g;
+  const int H_kv = d.num_kv_heads;
+  const int64_t elt = elt_bytes(&d);
+  int num_cus = (opts && opts->num_cus > 0) ? opts->num_cus : 256;
+
+  // ---- prefill tiles: requests whose qo * g rows exceed one decode unit
+  const int T = std::max(1, pdk::kPrefillRows / g);  // tokens per tile
+  struct Tile {
+    pdk::PrefillItem it;
+    int64_t cost;
+  };
+  std::vector<std::vector<Tile>> groups;  // per (request, kv head)
+  for (int r = 0; r < P.B; ++r) {
+    const pdk::ReqInfo& ri = P.req[r];
+    if (ri.qo == 0 || (int64_t)ri.qo * g <= pdk::kDecodeCols) continue;
+    const int64_t pairs = (int64_t)ri.qo * (ri.kv - ri.qo) + (int64_t)ri.qo * (ri.qo + 1) / 2;
+    P.prefill_flops += 4LL * d.head_dim * d.num_qo_heads * (d.causal ? pairs : (int64_t)ri.qo * ri.kv);
+    for (int hk = 0; hk < H_kv; ++hk) {
+      std::vector<Tile> grp;
+      for (int q0 = 0; q0 < ri.qo; q0 += T) {
+        const int nq = std::min(T, ri.qo - q0);
+        const int kv_end = d.causal ? ri.kv - ri.qo + q0 + nq : ri.kv;
+        grp.push_back({{r, hk, q0, nq, kv_end, 0, 0, 0}, (int64_t)nq * g * kv_end});
+      }
+      groups.push_back(std::move(grp));
+    }
+  }
+  if (!groups.empty()) {
+    // groups -> XCDs (largest group to the least loaded XCD), then tiles in
+    // dispatch order: slot i runs on XCD i % 8, longest tiles first.
+    std::vector<int> order(groups.size());
+    std::vector<int64_t> gcost(groups.size(), 0);
+    for (size_t i = 0; i < groups.size(); ++i) {
+      order[i] = (int)i;
+      for (auto& t : groups[i]) gcost[i] += t.cost;
+    }
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return gcost[a] > gcost[b]; });
+    std::vector<std::vector<Tile>> xq(kNumXcd);
+    std::vector<int64_t> xload(kNumXcd, 0);
+    for (int gi : order) {
+      int x = (int)(std::min_element(xload.begin(), xload.end()) - xload.begin());
+      xload[x] += gcost[gi];
+      for (auto& t : groups[gi]) xq[x].push_back(t);
+    }
+    size_t total = 0;
+    for (auto& q : xq) {
+      std::stable_sort(q.begin(), q.end(), [](const Tile& a, const Tile& b) { return a.cost > b.cost; });
+      total += q.size();
+    }
+    std::vector<size_t> head(kNumXcd, 0);
+    P.pf.reserve(total);
+    for (size_t i = 0; i < total; ++i) {
+      int x = (int)(i % kNumXcd);
+      if (head[x] >= xq[x].size()) {  // this XCD ran out: take from the fullest
+        size_t best = 0;
+        int bx = -1;
+        for (int y = 0; y < kNumXcd; ++y)
+          if (xq[y].size() - head[y] > best) best = xq[y].size() - head[y], bx = y;
+        x = bx;
+      }
+      P.pf.push_back(xq[x][head[x]++].it);
+    }
+  }
+
+  // ---- decode units: requests with qo * g <= 16
+  int64_t decode_keys = 0;
+  for (int r = 0; r < P.B; ++r) {
+    const pdk::ReqInfo& ri = P.req[r];
+    if (ri.qo == 0 || (int64_t)ri.qo * g > pdk::kDecodeCols) continue;
+    decode_keys += (int64_t)ri.kv * H_kv;
+    P.decode_bytes += 2LL * ri.kv * H_kv * d.head_dim * elt;
+  }
+  int chunk = 0;
+  if (opts && opts->decode_chunk_keys > 0) {
+    chunk = (opts->decode_chunk_keys + 31) / 32 * 32;
+  } else if (decode_keys > 0) {
+    const int64_t target_units = (int64_t)num_cus * 16;
+    int64_t c = (decode_keys + target_units - 1) / target_units;
+    c = (c + 255) / 256 * 256;
+    chunk = (int)std::min<int64_t>(std::max<int64_t>(c, 256), 16384);
+  }
+  P.chunk_keys = chunk;
+  std::vector<pdk::DecodeItem> units;
+  for (int r = 0; r < P.B; ++r) {
+    const pdk::ReqInfo& ri = P.req[r];
+    if (ri.qo == 0 || (int64_t)ri.qo * g > pdk::kDecodeCols) continue;
+    int nch = (ri.kv + chunk - 1) / chunk;
+    int len = (ri.kv + nch - 1) / nch;
+    len = (len + 31) / 32 * 32;
+    nch = (ri.kv + len - 1) / len;
+    for (int hk = 0; hk < H_kv; ++hk) {
+      P.mg.push_back({r, hk, P.n_parts, nch});
+      for (int c = 0; c < nch; ++c) {
+        const int k0 = c * len, k1 = std::min(ri.kv, k0 + len);
+        units.push_back({r, hk, k0, k1, P.n_parts++, 0, 0, 0});
+      }
+    }
+  }
+  std::stable_sort(units.begin(), units.end(), [](const pdk::DecodeItem& a, const pdk::DecodeItem& b) {
+    return (a.k1 - a.k0) > (b.k1 - b.k0);
+  });
+  P.du = std::move(units);
+
+  // ---- workspace layout
+  size_t off = 0;
+  P.off_qo = off;
+  off = align_up(off + sizeof(int32_t) * (P.B + 1));
+  P.off_req = off;
+  off = align_up(off + sizeof(pdk::ReqInfo) * P.B);
+  P.off_pages = off;
+  off = align_up(off + sizeof(int32_t) * P.pages.size());
+  P.off_pf = off;
+  off = align_up(off + sizeof(pdk::PrefillItem) * P.pf.size());
+  P.off_du = off;
+  off = align_up(off + sizeof(pdk::DecodeItem) * P.du.size());
+  P.off_mg = off;
+  off = align_up(off + sizeof(pdk::MergeGroup) * P.mg.size());
+  P.meta_bytes = off;
+  P.off_part_o = off;
+  off = align_up(off + sizeof(float) * (size_t)P.n_parts * pdk::kDecodeCols * d.head_dim);
+  P.off_part_lse = off;
+  off = align_up(off + sizeof(float) * (size_t)P.n_parts * pdk::kDecodeCols);
+  P.ws_bytes = off;
+
+  P.blob.assign(P.meta_bytes, 0);
+  auto put = [&](size_t o, const void* src, size_t n) {
+    if (n) std::memcpy(P.blob.data() + o, src, n);
+  };
+  put(P.off_qo, P.qo_indptr.data(), sizeof(int32_t) * P.qo_indptr.size());
+  put(P.off_req, P.req.data(), sizeof(pdk::ReqInfo) * P.req.size());
+  put(P.off_pages, P.pages.data(), sizeof(int32_t) * P.pages.size());
+  put(P.off_pf, P.pf.data(), sizeof(pdk::PrefillItem) * P.pf.size());
+  put(P.off_du, P.du.data(), sizeof(pdk::DecodeItem) * P.du.size());
+  put(P.off_mg, P.mg.data(), sizeof(pdk::MergeGroup) * P.mg.size());
+  return PD_OK;
+}
+
+pdk::AttnParams attn_params(const pd_plan_s& P, void* d_ws) {
+  char* ws = (char*)d_ws;
+  pdk::AttnParams a{};
+  a.qo_indptr = (const int32_t*)(ws + P.off_qo);
+  a.req = (const pdk::ReqInfo*)(ws + P.off_req);
+  a.page_indices = (const int32_t*)(ws + P.off_pages);
+  a.pf = (const pdk::PrefillItem*)(ws + P.off_pf);
+  a.du = (const pdk::DecodeItem*)(ws + P.off_du);
+  a.mg = (const pdk::MergeGroup*)(ws + P.off_mg);
+  a.part_o = (float*)(ws + P.off_part_o);
+  a.part_lse = (float*)(ws + P.off_part_lse);
+  a.n_pf = (int32_t)P.pf.size();
+  a.n_du = (int32_t)P.du.size();
+  a.n_mg = (int32_t)P.mg.size();
+  a.B = P.B;
+  a.H_q = P.desc.num_qo_heads;
+  a.H_kv = P.desc.num_kv_heads;
+  a.g = P.g;
+  a.ps = P.desc.page_size;
+  a.D = P.desc.head_dim;
+  a.causal = P.desc.causal;
+  a.sm_scale = P.desc.sm_scale;
+  a.c_log2 = P.desc.sm_scale * 1.4426950408889634f;
+  a.page_elems = 2LL * P.desc.num_kv_heads * P.desc.page_size * P.desc.head_dim;
+  return a;
+}
+
+pd_status hip_fail(hipError_t e, const char* what) {
+  return fail(PD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+pd_status check_page_list(const pd_attn_desc* desc, int32_t num_pool_pages, const int32_t* ids,
+                          int32_t n, size_t buf_bytes, size_t scratch_bytes, const void* pool,
+                          const void* buf, const void* scratch) {
+  pd_status s = check_desc(desc);
+  if (s != PD_OK) return s;
+  if (n < 0) return fail(PD_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return PD_OK;
+  if (!ids || !pool || !buf || !scratch) return fail(PD_ERR_INVALID_ARG, "NULL pointer argument");
+  if (num_pool_pages < 1) return fail(PD_ERR_INVALID_ARG, "num_pool_pages must be >= 1");
+  if (buf_bytes < (size_t)n * (size_t)page_bytes_of(desc))
+    return fail(PD_ERR_WORKSPACE, "buffer smaller than n pages");
+  if (scratch_bytes < sizeof(int32_t) * (size_t)n)
+    return fail(PD_ERR_WORKSPACE, "scratch smaller than 4 * n bytes");
+  std::vector<uint8_t> seen((size_t)num_pool_pages, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= num_pool_pages)
+      return fail(PD_ERR_OUT_OF_RANGE, "page id " + std::to_string(ids[i]) + " outside the pool");
+    if (seen[ids[i]]) return fail(PD_ERR_INVALID_ARG, "page id " + std::to_string(ids[i]) + " repeated");
+    seen[ids[i]] = 1;
+  }
+  return PD_OK;
+}
+
+pd_status pack_common(const pd_attn_desc* desc, const void* src, void* dst, int32_t num_pool_pages,
+                      const int32_t* ids, int32_t n, size_t buf_bytes, void* scratch,
+                      size_t scratch_bytes, void* stream, bool to_buffer) {
+  pd_status s = check_page_list(desc, num_pool_pages, ids, n, buf_bytes, scratch_bytes,
+                                to_buffer ? src : dst, to_buffer ? dst : src, scratch);
+  if (s != PD_OK || n == 0) return s;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(scratch, ids, sizeof(int32_t) * (size_t)n, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "page id upload");
+  pdk::PackParams p{};
+  p.dst = dst;
+  p.src = src;
+  p.page_ids = (const int32_t*)scratch;
+  p.n = n;
+  p.to_buffer = to_buffer ? 1 : 0;
+  p.page_bytes = page_bytes_of(desc);
+  e = pdk::launch_pack(p, st);
+  if (e != hipSuccess) return hip_fail(e, to_buffer ? "pack launch" : "unpack launch");
+  return PD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pd_status pd_plan(const pd_attn_desc* desc, int32_t batch, const int32_t* qo_lens, const int32_t* kv_lens,
+                  const int32_t* page_indptr, const int32_t* page_indices, int32_t num_pool_pages,
+                  const pd_plan_options* opts, pd_plan_t* out) {
+  try {
+    if (!out) return fail(PD_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    pd_status s = check_desc(desc);
+    if (s != PD_OK) return s;
+    if (batch < 1) return fail(PD_ERR_INVALID_ARG, "batch must be >= 1");
+    if (!qo_lens || !kv_lens || !page_indptr) return fail(PD_ERR_INVALID_ARG, "NULL length or indptr array");
+    if (num_pool_pages < 0) return fail(PD_ERR_INVALID_ARG, "num_pool_pages must be >= 0");
+    if (opts && (opts->decode_chunk_keys < 0 || opts->num_cus < 0))
+      return fail(PD_ERR_INVALID_ARG, "negative planner option");
+    const int ps = desc->page_size;
+    if (page_indptr[0] != 0) return fail(PD_ERR_INVALID_ARG, "page_indptr[0] must be 0");
+    int64_t rows = 0;
+    for (int r = 0; r < batch; ++r) {
+      const int32_t qo = qo_lens[r], kv = kv_lens[r];
+      if (qo < 0 || kv < 0) return fail(PD_ERR_INVALID_ARG, "request " + std::to_string(r) + ": negative length");
+      if (qo > kv)
+        return fail(PD_ERR_INVALID_ARG, "request " + std::to_string(r) + ": qo_len > kv_len (the new tokens are part of the cache)");
+      const int64_t need = ((int64_t)kv + ps - 1) / ps;
+      const int64_t have = (int64_t)page_indptr[r + 1] - page_indptr[r];
+      if (have != need)
+        return fail(PD_ERR_INVALID_ARG, "request " + std::to_string(r) + ": has " + std::to_string(have) +
+                                            " pages, needs ceil(kv_len / page_size) = " + std::to_string(need));
+      rows += qo;
+    }
+    if (rows > INT32_MAX) return fail(PD_ERR_INVALID_ARG, "too many query rows");
+    const int64_t total_pages = page_indptr[batch];
+    if (total_pages > 0 && !page_indices) return fail(PD_ERR_INVALID_ARG, "page_indices is NULL");
+    {
+      std::vector<uint8_t> seen((size_t)std::max(num_pool_pages, 1), 0);
+      for (int64_t i = 0; i < total_pages; ++i) {
+        const int32_t id = page_indices[i];
+        if (id < 0 || id >= num_pool_pages)
+          return fail(PD_ERR_OUT_OF_RANGE, "page id " + std::to_string(id) + " outside the pool");
+        if (seen[id]) return fail(PD_ERR_INVALID_ARG, "page id " + std::to_string(id) + " appears twice");
+        seen[id] = 1;
+      }
+    }
+    pd_plan_s* P = new pd_plan_s();
+    P->desc = *desc;
+    P->B = batch;
+    P->g = desc->num_qo_heads / desc->num_kv_heads;
+    P->total_rows = (int32_t)rows;
+    P->qo_indptr.resize(batch + 1);
+    P->req.resize(batch);
+    P->qo_indptr[0] = 0;
+    for (int r = 0; r < batch; ++r) {
+      P->req[r] = {P->qo_indptr[r], qo_lens[r], kv_lens[r], page_indptr[r]};
+      P->qo_indptr[r + 1] = P->qo_indptr[r] + qo_lens[r];
+    }
+    P->pages.assign(page_indices, page_indices + total_pages);
+    s = build_plan(*P, opts);
+    if (s != PD_OK) {
+      delete P;
+      return s;
+    }
+    *out = P;
+    return PD_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(PD_ERR_NO_MEMORY, "host allocation failed");
+  } catch (...) {
+    return fail(PD_ERR_INVALID_ARG, "unexpected error while planning");
+  }
+}
+
+size_t pd_plan_workspace_bytes(pd_plan_t plan) { return plan ? plan->ws_bytes : 0; }
+
+pd_status pd_plan_get_stats(pd_plan_t plan, pd_plan_stats* out) {
+  if (!plan || !out) return fail(PD_ERR_INVALID_ARG, "NULL argument");
+  out->batch = plan->B;
+  out->total_q_rows = plan->total_rows;
+  out->prefill_tiles = (int32_t)plan->pf.size();
+  out->decode_units = (int32_t)plan->du.size();
+  out->decode_row_groups = (int32_t)plan->mg.size();
+  out->decode_chunk_keys = plan->chunk_keys;
+  out->prefill_flops = plan->prefill_flops;
+  out->decode_kv_bytes = plan->decode_bytes;
+  out->workspace_bytes = (int64_t)plan->ws_bytes;
+  return PD_OK;
+}
+
+int32_t pd_plan_work_items(pd_plan_t plan, int32_t kind, int32_t* out, int32_t max_items) {
+  if (!plan) return fail(PD_ERR_INVALID_ARG, "NULL plan");
+  const int32_t* src;
+  size_t count, width;
+  switch (kind) {
+    case 0: src = (const int32_t*)plan->pf.data(); count = plan->pf.size(); width = 8; break;
+    case 1: src = (const int32_t*)plan->du.data(); count = plan->du.size(); width = 8; break;
+    case 2: src = (const int32_t*)plan->mg.data(); count = plan->mg.size(); width = 4; break;
+    default: return fail(PD_ERR_INVALID_ARG, "unknown work item kind");
+  }
+  if (max_items > 0 && out) {
+    const size_t n = std::min(count, (size_t)max_items);
+    std::memcpy(out, src, n * width * sizeof(int32_t));
+  }
+  return (int32_t)count;
+}
+
+pd_status pd_plan_upload(pd_plan_t plan, void* d_ws, size_t ws_bytes, void* stream) {
+  try {
+    if (!plan || !d_ws) return fail(PD_ERR_INVALID_ARG, "NULL plan or workspace");
+    if (ws_bytes < plan->ws_bytes)
+      return fail(PD_ERR_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, plan needs " +
+                                        std::to_string(plan->ws_bytes));
+    hipError_t e;
+    if (!plan->pinned) {
+      e = hipHostMalloc(&plan->pinned, std::max<size_t>(plan->meta_bytes, kAlign), hipHostMallocDefault);
+      if (e != hipSuccess) {
+        plan->pinned = nullptr;
+        return hip_fail(e, "pinned staging allocation");
+      }
+      e = hipEventCreateWithFlags(&plan->ev, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(e, "event creation");
+    } else if (plan->ev_recorded) {
+      e = hipEventSynchronize(plan->ev);  // the previous upload still reads the staging buffer
+      if (e != hipSuccess) return hip_fail(e, "waiting for the previous upload");
+    }
+    std::memcpy(plan->pinned, plan->blob.data(), plan->meta_bytes);
+    hipStream_t st = (hipStream_t)stream;
+    e = hipMemcpyAsync(d_ws, plan->pinned, plan->meta_bytes, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "workspace upload");
+    e = hipEventRecord(plan->ev, st);
+    if (e != hipSuccess) return hip_fail(e, "event record");
+    plan->ev_recorded = true;
+    return PD_OK;
+  } catch (...) {
+    return fail(PD_ERR_HIP, "unexpected error in upload");
+  }
+}
+
+void pd_plan_free(pd_plan_t plan) {
+  if (!plan) return;
+  if (plan->ev) {
+    if (plan->ev_recorded) (void)hipEventSynchronize(plan->ev);
+    (void)hipEventDestroy(plan->ev);
+  }
+  if (plan->pinned) (void)hipHostFree(plan->pinned);
+  delete plan;
+}
+
+pd_status pd_kv_append(pd_plan_t plan, void* d_ws, void* kv_pool, const void* k_new, const void* v_new,
+                       void* stream) {
+  if (!plan || !d_ws) return fail(PD_ERR_INVALID_ARG, "NULL plan or workspace");
+  if (plan->total_rows == 0) return PD_OK;
+  if (!kv_pool || !k_new || !v_new) return fail(PD_ERR_INVALID_ARG, "NULL pool or K/V pointer");
+  char* ws = (char*)d_ws;
+  pdk::AppendParams p{};
+  p.pool = kv_pool;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.qo_indptr = (const int32_t*)(ws + plan->off_qo);
+  p.req = (const pdk::ReqInfo*)(ws + plan->off_req);
+  p.page_indices = (const int32_t*)(ws + plan->off_pages);
+  p.B = plan->B;
+  p.total_rows = plan->total_rows;
+  p.H_kv = plan->desc.num_kv_heads;
+  p.ps = plan->desc.page_size;
+  p.D = plan->desc.head_dim;
+  p.elt = elt_bytes(&plan->desc);
+  hipError_t e = pdk::launch_append(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return PD_OK;
+}
+
+pd_status pd_attention_run(pd_plan_t plan, void* d_ws, const void* q, const void* kv_pool, float* out,
+                           float* lse, void* stream) {
+  if (!plan || !d_ws) return fail(PD_ERR_INVALID_ARG, "NULL plan or workspace");
+  if (plan->total_rows == 0) return PD_OK;
+  if (!q || !kv_pool || !out) return fail(PD_ERR_INVALID_ARG, "NULL q, pool or out");
+  pdk::AttnParams a = attn_params(*plan, d_ws);
+  a.q = q;
+  a.pool = kv_pool;
+  a.out = out;
+  a.lse = lse;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = pdk::launch_attention(a, plan->desc.dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  e = pdk::launch_merge(a, st);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return PD_OK;
+}
+
+size_t pd_kv_pack_bytes(const pd_attn_desc* desc, int32_t n_pages) {
+  if (n_pages < 0 || !desc) return 0;
+  if (desc->num_kv_heads < 1 || desc->page_size < 1 || desc->head_dim < 1) return 0;
+  if (desc->dtype != PD_F32 && desc->dtype != PD_BF16) return 0;
+  return (size_t)n_pages * (size_t)page_bytes_of(desc);
+}
+
+pd_status pd_kv_pack(const pd_attn_desc* desc, const void* kv_pool, int32_t num_pool_pages,
+                     const int32_t* page_ids, int32_t n, void* d_buf, size_t buf_bytes, void* d_scratch,
+                     size_t scratch_bytes, void* stream) {
+  try {
+    return pack_common(desc, kv_pool, d_buf, num_pool_pages, page_ids, n, buf_bytes, d_scratch,
+                       scratch_bytes, stream, true);
+  } catch (...) {
+    return fail(PD_ERR_NO_MEMORY, "host allocation failed");
+  }
+}
+
+pd_status pd_kv_unpack(const pd_attn_desc* desc, void* kv_pool, int32_t num_pool_pages,
+                       const int32_t* page_ids, int32_t n, const void* d_buf, size_t buf_bytes,
+                       void* d_scratch, size_t scratch_bytes, void* stream) {
+  try {
+    return pack_common(desc, d_buf, kv_pool, num_pool_pages, page_ids, n, buf_bytes, d_scratch,
+                       scratch_bytes, stream, false);
+  } catch (...) {
+    return fail(PD_ERR_NO_MEMORY, "host allocation failed");
+  }
+}
+
+const char* pd_status_string(pd_status s) {
+  switch (s) {
+    case PD_OK: return "PD_OK";
+    case PD_ERR_INVALID_ARG: return "PD_ERR_INVALID_ARG";
+    case PD_ERR_UNSUPPORTED: return "PD_ERR_UNSUPPORTED";
+    case PD_ERR_OUT_OF_RANGE: return "PD_ERR_OUT_OF_RANGE";
+    case PD_ERR_WORKSPACE: return "PD_ERR_WORKSPACE";
+    case PD_ERR_HIP: return "PD_ERR_HIP";
+    case PD_ERR_NO_MEMORY: return "PD_ERR_NO_MEMORY";
+  }
+  return "unknown pd_status";
+}
+
+const char* pd_last_error(void) { return g_last_error.c_str(); }
+
+const char* pd_version(void) { return "pd_attn 0.1.0 (gfx950)"; }
+
+}  // extern "C"

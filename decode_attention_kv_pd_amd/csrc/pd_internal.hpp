@@ -1,0 +1,89 @@
+// Internal types shared by the host runtime (api.cpp) and the HIP kernels
+// (kernels.hip).  Not part of the public ABI (include/pd_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pdk {
+
+// Per-request row of the device tables.
+struct ReqInfo {
+  int32_t qo_start;    // first query row of the request in q / out
+  int32_t qo;          // new query rows
+  int32_t kv;          // cached tokens including the new ones
+  int32_t page_start;  // first entry of the request in page_indices
+};
+
+// A causal query tile of a prefill request, computed by one 256-thread block
+// on bf16 MFMA: tokens [q0, q0 + nq) of request `req` times the g query heads
+// of KV head `hk` (row n of the tile = token q0 + n / g, head hk * g + n % g),
+// over keys [0, kv_end).  Written straight to out / lse.
+struct PrefillItem {
+  int32_t req, hk, q0, nq, kv_end, rsv0, rsv1, rsv2;
+};
+
+// A split-KV decode unit, computed by one wavefront: all qo * g (<= 16) query
+// rows of (request, KV head) over keys [k0, k1).  Writes a partial result
+// (normalised o and its log-sum-exp) to slot `part`.
+struct DecodeItem {
+  int32_t req, hk, k0, k1, part, rsv0, rsv1, rsv2;
+};
+
+// The partial results [part0, part0 + nparts) of one (request, KV head) are
+// merged into out / lse by the merge kernel.
+struct MergeGroup {
+  int32_t req, hk, part0, nparts;
+};
+
+constexpr int kBlockThreads = 256;  // both roles of the attention kernel
+constexpr int kPrefillRows = 128;   // query rows per prefill tile
+constexpr int kDecodeCols = 16;     // query rows per decode unit (MFMA N)
+constexpr int kWavesPerBlock = 4;
+
+struct AttnParams {
+  const void* q;
+  const void* pool;
+  float* out;
+  float* lse;  // may be null
+  const int32_t* qo_indptr;
+  const ReqInfo* req;
+  const int32_t* page_indices;
+  const PrefillItem* pf;
+  const DecodeItem* du;
+  const MergeGroup* mg;
+  float* part_o;    // [n_du][kDecodeCols][D]
+  float* part_lse;  // [n_du][kDecodeCols]
+  int32_t n_pf, n_du, n_mg, B;
+  int32_t H_q, H_kv, g, ps;
+  int32_t D, causal;
+  float sm_scale;
+  float c_log2;        // sm_scale * log2(e)
+  int64_t page_elems;  // elements of one page: 2 * H_kv * ps * D
+};
+
+struct AppendParams {
+  void* pool;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* qo_indptr;  // [B + 1]
+  const ReqInfo* req;
+  const int32_t* page_indices;
+  int32_t B, total_rows, H_kv, ps, D, elt;
+};
+
+struct PackParams {
+  void* dst;
+  const void* src;
+  const int32_t* page_ids;  // device
+  int32_t n;
+  int32_t to_buffer;  // 1: pool -> buffer (pack), 0: buffer -> pool (unpack)
+  int64_t page_bytes;
+};
+
+hipError_t launch_attention(const AttnParams& p, int dtype, hipStream_t s);
+hipError_t launch_merge(const AttnParams& p, hipStream_t s);
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_pack(const PackParams& p, hipStream_t s);
+
+}  // namespace pdk

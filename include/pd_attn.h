@@ -1,0 +1,258 @@
+/*
+ * pd_attn.h -- C ABI of the MI355X (gfx950) ragged paged-attention library
+ * libpd_attn.so.
+ *
+ * The library runs the attention hot path behind disaggregated prefill and
+ * decode on one GPU:
+ *   pd_plan          split a ragged batch of requests into GPU work
+ *   pd_kv_append     write each request's new K/V rows into its pages
+ *   pd_attention_run causal prefill rows and decode rows in one launch, then
+ *                    the merge of split-KV partial results
+ *   pd_kv_pack       gather whole pages into one contiguous transfer buffer
+ *   pd_kv_unpack     scatter such a buffer into (other) pages
+ *
+ * What the operations compute follows the Perplexity post "Disaggregated
+ * prefill and decode" and the kwkr.cn PD-disaggregation survey; each entry
+ * point names the passage it follows.  The attention itself is standard
+ * scaled-dot-product softmax attention:
+ *   for request r with qo new query rows over kv cached keys, query row i sits
+ *   at absolute position p = kv - qo + i and (when causal) sees keys j <= p;
+ *   query head h reads KV head h / g, g = num_qo_heads / num_kv_heads;
+ *   O[i,h] = sum_j softmax_j(sm_scale * <Q[i,h], K[j,h/g]>) V[j,h/g]
+ *   LSE[i,h] = ln sum_j exp(sm_scale * <Q[i,h], K[j,h/g]>)   (natural log)
+ *
+ * Memory layouts (all row-major, C order):
+ *   KV pool   [num_pool_pages][2][num_kv_heads][page_size][head_dim] elements
+ *             (K half then V half of each page; "HND": heads before tokens,
+ *             so a page, and each head's slice of it, is contiguous -- post,
+ *             section "Sharded KV Cache Transfers").  Token t of request r is
+ *             in page page_indices[page_indptr[r] + t / page_size] at slot
+ *             t % page_size.
+ *   q         [sum qo][num_qo_heads][head_dim], requests back to back
+ *   k_new,
+ *   v_new     [sum qo][num_kv_heads][head_dim], requests back to back
+ *   out       [sum qo][num_qo_heads][head_dim] float32
+ *   lse       [sum qo][num_qo_heads] float32
+ *   element type: float32 (PD_F32) or bfloat16 (PD_BF16) for the pool, q,
+ *   k_new and v_new; out and lse are always float32 (fp32 accumulation).
+ *
+ * Ownership: the caller allocates and owns every device buffer (pool, q,
+ * k_new, v_new, out, lse, workspace, pack buffer, scratch); the library never
+ * allocates or frees device memory.  The library owns the opaque plan (host
+ * memory and a pinned staging buffer), released by pd_plan_free.  A plan is
+ * immutable once built; pd_plan_upload may be called again on another
+ * workspace.
+ *
+ * Streams: every `void* stream` is a hipStream_t (NULL = the default stream);
+ * all device work is enqueued on it and no call except pd_plan_free waits for
+ * the device.
+ *
+ * Errors: every argument is checked before anything is enqueued, so a failing
+ * call has no side effect on device memory.  Calls return PD_OK or a negative
+ * pd_status; pd_last_error() gives a message for the calling thread's last
+ * failure.  No C++ exception crosses this interface.
+ */
+#ifndef PD_ATTN_H_
+#define PD_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pd_status {
+  PD_OK = 0,
+  PD_ERR_INVALID_ARG = -1,  /* malformed lengths, page table, null pointer */
+  PD_ERR_UNSUPPORTED = -2,  /* head_dim, page_size, dtype or group size the
+                               kernels do not implement */
+  PD_ERR_OUT_OF_RANGE = -3, /* page id outside the pool */
+  PD_ERR_WORKSPACE = -4,    /* workspace / buffer / scratch too small */
+  PD_ERR_HIP = -5,          /* a HIP runtime call or kernel launch failed */
+  PD_ERR_NO_MEMORY = -6     /* host allocation failed */
+} pd_status;
+
+typedef enum pd_dtype { PD_F32 = 0, PD_BF16 = 1 } pd_dtype;
+
+/* Shape of one attention layer.
+ *   num_qo_heads  query heads H_q (> 0, multiple of num_kv_heads)
+ *   num_kv_heads  KV heads H_kv (> 0); g = H_q / H_kv <= 16 is required for
+ *                 single-token (decode) rows, larger groups are supported
+ *                 for prefill rows only
+ *   head_dim      64 or 128
+ *   page_size     16, 32, 64 or 128 tokens per page
+ *   dtype         pd_dtype of pool, q, k_new, v_new
+ *   causal        1: end-aligned causal mask; 0: every row sees all kv keys
+ *   sm_scale      softmax scale applied to <q, k> (usually 1/sqrt(head_dim)) */
+typedef struct pd_attn_desc {
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t dtype;
+  int32_t causal;
+  float sm_scale;
+} pd_attn_desc;
+
+/* Optional planner controls (NULL = defaults).
+ *   decode_chunk_keys  keys per split-KV chunk of a decode row group; 0 lets
+ *                      the planner choose; otherwise rounded up to 32
+ *   num_cus            compute units to balance over; 0 = 256 (MI355X)    */
+typedef struct pd_plan_options {
+  int32_t decode_chunk_keys;
+  int32_t num_cus;
+  int32_t reserved[6];
+} pd_plan_options;
+
+/* Plan statistics (pd_plan_get_stats). */
+typedef struct pd_plan_stats {
+  int32_t batch;
+  int32_t total_q_rows;        /* sum qo */
+  int32_t prefill_tiles;       /* MFMA query tiles (rows of prefill requests) */
+  int32_t decode_units;        /* split-KV units (one wavefront each) */
+  int32_t decode_row_groups;   /* (request, kv head) groups merged */
+  int32_t decode_chunk_keys;   /* chunk length used */
+  int64_t prefill_flops;       /* 4 * head_dim * visible (query, key) pairs * H_q / g ... summed exactly */
+  int64_t decode_kv_bytes;     /* K + V bytes the decode rows read */
+  int64_t workspace_bytes;
+} pd_plan_stats;
+
+typedef struct pd_plan_s* pd_plan_t;
+
+/* Build a plan for one step of a ragged batch.  Host only, synchronous; no
+ * HIP call is made.
+ *   batch          number of requests B (>= 1)
+ *   qo_lens[B]     new query tokens of each request (>= 0; 0 = no rows)
+ *   kv_lens[B]     cached tokens of each request *including* the new ones
+ *                  (0 <= qo <= kv): the new rows are appended at positions
+ *                  [kv - qo, kv) before attention reads [0, kv)
+ *   page_indptr[B+1], page_indices[page_indptr[B]]
+ *                  CSR page table; request r owns exactly ceil(kv_r /
+ *                  page_size) pages, in token order; every id is in
+ *                  [0, num_pool_pages) and no id appears twice
+ *   opts           may be NULL
+ *   out            receives the plan (release with pd_plan_free)
+ * Follows the post's statement of the problem (section "Prefill vs Decode
+ * performance"): each step batches prefill requests (many query tokens,
+ * compute bound) with decode requests (qo_len = 1, bound by reading the
+ * kv_len-long cache), and attention is spread over both the requests and
+ * their kv_len to keep the device busy.  Rows of requests with qo * g <= 16
+ * become split-KV decode units; the rest become causal MFMA query tiles.
+ * Errors: PD_ERR_INVALID_ARG (null pointers, batch < 1, negative lengths,
+ * qo > kv, wrong page count, duplicate page id, H_q % H_kv != 0),
+ * PD_ERR_OUT_OF_RANGE (page id outside the pool), PD_ERR_UNSUPPORTED
+ * (head_dim, page_size, dtype), PD_ERR_NO_MEMORY. */
+pd_status pd_plan(const pd_attn_desc* desc, int32_t batch,
+                  const int32_t* qo_lens, const int32_t* kv_lens,
+                  const int32_t* page_indptr, const int32_t* page_indices,
+                  int32_t num_pool_pages, const pd_plan_options* opts,
+                  pd_plan_t* out);
+
+/* Device workspace bytes the plan needs (page table, work lists, split-KV
+ * partial results).  0 for a NULL plan. */
+size_t pd_plan_workspace_bytes(pd_plan_t plan);
+
+/* Copy the plan's tables into the caller's device workspace (asynchronous
+ * host-to-device copy from the plan's pinned staging buffer on `stream`).
+ * Must precede pd_kv_append / pd_attention_run with the same d_ws.
+ * Errors: PD_ERR_INVALID_ARG (null plan / d_ws), PD_ERR_WORKSPACE
+ * (ws_bytes < pd_plan_workspace_bytes), PD_ERR_HIP. */
+pd_status pd_plan_upload(pd_plan_t plan, void* d_ws, size_t ws_bytes,
+                         void* stream);
+
+/* Statistics of a plan (host only). */
+pd_status pd_plan_get_stats(pd_plan_t plan, pd_plan_stats* out);
+
+/* Diagnostics: copy the plan's work list (host only).
+ *   kind 0: prefill tiles, 8 int32 each:
+ *           {request, kv_head, first token, tokens, key end (exclusive), 0,0,0}
+ *           in launch order (block i of the launch runs on XCD i % 8)
+ *   kind 1: decode units, 8 int32 each:
+ *           {request, kv_head, key begin, key end (exclusive), partial slot,
+ *            0,0,0} in launch order (four units per block)
+ *   kind 2: merge groups, 4 int32 each:
+ *           {request, kv_head, first partial slot, partial count}
+ * Writes at most max_items items to out (which may be NULL when max_items is
+ * 0) and returns the total number of items of that kind, or a negative
+ * pd_status (PD_ERR_INVALID_ARG for a NULL plan or an unknown kind). */
+int32_t pd_plan_work_items(pd_plan_t plan, int32_t kind, int32_t* out,
+                           int32_t max_items);
+
+/* Release a plan; waits for its last upload to finish.  NULL is a no-op. */
+void pd_plan_free(pd_plan_t plan);
+
+/* Append the step's new K and V rows into the pool: for each request r and
+ * i < qo_r, row i of its k_new / v_new block goes to token position
+ * kv_r - qo_r + i.  Bit-exact copy; touches no other slot.  The post's
+ * section "KV Messenger": KV entries are appended to the cache layer by
+ * layer and are valid after the append and before attention.
+ *   d_ws    workspace the plan was uploaded to
+ *   kv_pool device pool (layout above)
+ *   k_new, v_new  device [sum qo][num_kv_heads][head_dim]
+ * Errors: PD_ERR_INVALID_ARG (null pointer), PD_ERR_HIP. */
+pd_status pd_kv_append(pd_plan_t plan, void* d_ws, void* kv_pool,
+                       const void* k_new, const void* v_new, void* stream);
+
+/* Attention of every query row of the plan over its request's cache [0, kv).
+ * Prefill tiles and decode units run in one launch; a second launch merges
+ * the decode units' split-KV partial results (log-sum-exp weighted, fixed
+ * order, so a fixed plan gives bitwise-reproducible output).  The post's
+ * section "Prefill vs Decode performance" (prefill and decode requests
+ * batched together; attention parallel over requests and kv_len) and the
+ * kwkr.cn survey, section 8 (a prefill chunk attends over all earlier KV).
+ *   q        device [sum qo][num_qo_heads][head_dim]
+ *   kv_pool  device pool after pd_kv_append
+ *   out      device float32 [sum qo][num_qo_heads][head_dim]
+ *   lse      device float32 [sum qo][num_qo_heads], or NULL
+ * Tail slots of a request's last page and pages outside its list are never
+ * read.  Errors: PD_ERR_INVALID_ARG (null pointer), PD_ERR_HIP. */
+pd_status pd_attention_run(pd_plan_t plan, void* d_ws, const void* q,
+                           const void* kv_pool, float* out, float* lse,
+                           void* stream);
+
+/* Bytes of n packed pages: n * 2 * num_kv_heads * page_size * head_dim *
+ * element size.  0 on a bad descriptor or n < 0. */
+size_t pd_kv_pack_bytes(const pd_attn_desc* desc, int32_t n_pages);
+
+/* Gather whole pages, in list order, into one contiguous buffer of verbatim
+ * page images (bit-exact).  The post's sections "KV Messenger" and "Sharded
+ * KV Cache Transfers": transfers are per page, each HND page being one
+ * contiguous write, and their number is proportional to the pages moved; a
+ * request's whole page list at once is the request-level transfer
+ * granularity of the kwkr.cn survey, section 5.4.
+ *   page_ids   HOST array of n page ids in [0, num_pool_pages), no repeats;
+ *              copied to d_scratch on `stream` before the call returns
+ *   d_buf      device buffer of buf_bytes >= pd_kv_pack_bytes(desc, n)
+ *   d_scratch  device scratch of scratch_bytes >= 4 * n
+ * Errors: PD_ERR_INVALID_ARG, PD_ERR_OUT_OF_RANGE, PD_ERR_WORKSPACE,
+ * PD_ERR_UNSUPPORTED, PD_ERR_HIP.  n == 0 is a no-op. */
+pd_status pd_kv_pack(const pd_attn_desc* desc, const void* kv_pool,
+                     int32_t num_pool_pages, const int32_t* page_ids,
+                     int32_t n, void* d_buf, size_t buf_bytes,
+                     void* d_scratch, size_t scratch_bytes, void* stream);
+
+/* Scatter a packed buffer: buffer page i is written verbatim to pool page
+ * page_ids[i].  The destination ids are the receiver's own pages and may
+ * differ from the ids the buffer was packed from (post, section "KV
+ * Messenger": the decoder allocates its pages before the transfer).
+ * Arguments and errors as pd_kv_pack. */
+pd_status pd_kv_unpack(const pd_attn_desc* desc, void* kv_pool,
+                       int32_t num_pool_pages, const int32_t* page_ids,
+                       int32_t n, const void* d_buf, size_t buf_bytes,
+                       void* d_scratch, size_t scratch_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* pd_status_string(pd_status s);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* pd_last_error(void);
+
+/* Library version string. */
+const char* pd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PD_ATTN_H_ */

@@ -1,0 +1,136 @@
+"""GPU: attention parity with the float64 oracle, element by element.
+
+Bars: max |O - O_oracle| <= 1e-4 for fp32 inputs and <= 2e-2 for bf16 inputs
+(fp32 accumulation); LSE within 1e-4 (fp32) / 2e-3 (bf16).  Cases span the
+five seeded workloads (the long one at reduced length here; full length in
+test_gpu_long), several tiles and ragged tails, every supported head_dim,
+page size and GQA group, causal and non-causal, qo = 0 requests, the
+decode/prefill boundary (qo * g = 16 / 17), and a sharpened softmax."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as OA
+from tests.harness import DeviceRun, oracle_outputs, report, tolerance
+from workloads import make_batch
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=None)
+def batch(wid, lengths=None, **kw):
+    if lengths is not None:
+        lengths = (list(lengths[0]), list(lengths[1]))
+    return make_batch(wid, lengths=lengths, **kw)
+
+
+def lse_tol(b):
+    return 1e-4 if b.dtype == "f32" else 2e-3
+
+
+def check(b, name, chunk=0):
+    print(f"case {name}: B={b.B} H={b.H_q}/{b.H_kv} D={b.D} ps={b.ps} {b.dtype} "
+          f"causal={b.causal} rows={int(b.qo_indptr[-1])} chunk={chunk}", flush=True)
+    out, lse = DeviceRun(b, decode_chunk_keys=chunk).step()
+    O, L = oracle_outputs(b)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    err = report(name, out, O)
+    assert err <= tolerance(b)
+    assert np.abs(lse - L).max() <= lse_tol(b)
+    return out, lse
+
+
+@pytest.mark.parametrize("wid", ["tiny", "decode", "prefill", "mixed"])
+def test_workload_parity(wid):
+    check(batch(wid), wid)
+
+
+RAGGED = [
+    # (workload for dtype/shape defaults, lengths, overrides)
+    ("tiny", ((1, 2, 3, 17, 64, 0), (1, 9, 40, 17, 64, 30)), {}),
+    ("tiny", ((4, 5, 1), (4, 70, 129)), dict(heads=(16, 4))),          # qo*g = 16 / 20 / 4
+    ("tiny", ((33, 1), (50, 100)), dict(causal=False)),
+    ("tiny", ((20, 1, 3), (100, 300, 31)), dict(head_dim=128, page_size=64)),
+    ("mixed", ((1, 2, 4, 5), (33, 65, 1000, 4000)), {}),                 # qo*g = 4 .. 20
+    ("mixed", ((1, 16, 17, 100), (1, 16, 17, 100)), dict(heads=(16, 16))),
+    ("mixed", ((1, 1, 200), (5000, 31, 1000)), dict(heads=(16, 1), page_size=128)),
+    ("mixed", ((300, 1, 3), (300, 777, 64)), dict(heads=(24, 8), page_size=32)),
+    ("mixed", ((129, 1), (257, 257)), dict(head_dim=64, page_size=64)),
+    ("mixed", ((70, 1, 2), (90, 333, 65)), dict(causal=False)),
+    ("prefill", ((513, 1), (1000, 1)), dict(heads=(8, 8))),
+    ("long", ((1000, 1, 1), (3000, 3000, 64)), dict(heads=(64, 8))),    # long at reduced size
+    ("long", ((48, 2), (96, 4100)), dict(heads=(128, 1), page_size=16)),  # g = 128
+]
+
+
+@pytest.mark.parametrize("idx", range(len(RAGGED)))
+def test_ragged_parity(idx):
+    wid, lengths, kw = RAGGED[idx]
+    check(batch(wid, lengths, **kw), f"ragged{idx}")
+
+
+def test_sharpened_softmax():
+    """Q scaled by 8: logits of order 8, far from uniform weights."""
+    check(batch("mixed", ((200, 1, 1), (260, 900, 33)), q_gain=8.0), "sharp")
+    check(batch("tiny", ((16, 1), (33, 40)), q_gain=8.0), "sharp_f32")
+
+
+@pytest.mark.parametrize("chunk", [32, 96, 512])
+def test_split_count_invariance(chunk):
+    b = batch("mixed", ((1, 2, 1, 3), (4000, 3000, 2048, 700)))
+    out0, _ = DeviceRun(b).step()
+    out1, _ = check(b, f"split{chunk}", chunk=chunk)
+    assert np.abs(out1 - out0).max() <= 2 * tolerance(b)
+
+
+def test_bitwise_deterministic_for_a_fixed_plan():
+    b = batch("mixed", ((300, 1, 1, 2), (300, 4000, 1500, 700)))
+    run = DeviceRun(b)
+    run.append()
+    run.attention()
+    torch.cuda.synchronize()
+    first = run.out.clone(), run.lse.clone()
+    for _ in range(3):
+        run.attention()
+    torch.cuda.synchronize()
+    assert torch.equal(first[0], run.out) and torch.equal(first[1], run.lse)
+
+
+def test_decode_step_equals_last_prefill_row():
+    """The held-back-token handoff (post, section "Speculative Decoding"): a
+    decode step over the cache of a prefill equals that prefill's last row."""
+    L = 777
+    full = batch("mixed", ((L,), (L,)))
+    dec = make_batch("mixed", lengths=([1], [L]))
+    dec.q = full.q[-1:].copy()
+    dec.k, dec.v = full.k, full.v
+    out_f, lse_f = DeviceRun(full).step()
+    out_d, lse_d = DeviceRun(dec).step()
+    O, L_ = OA.attend(full.to_f64(full.q[-1:]), full.to_f64(full.k), full.to_f64(full.v), [L - 1],
+                      full.sm_scale)
+    assert np.abs(out_d[0] - O[0]).max() <= tolerance(full)
+    assert np.abs(out_f[-1] - O[0]).max() <= tolerance(full)
+    assert np.abs(out_d[0] - out_f[-1]).max() <= 2 * tolerance(full)
+    assert np.abs(lse_d[0] - lse_f[-1]).max() <= 2 * lse_tol(full)
+
+
+def test_chunked_prefill_equals_full():
+    """Prefill in two chunks (the second attending over the first's KV)
+    equals one prefill (kwkr.cn survey, section 8)."""
+    L, c = 600, 250
+    full = batch("mixed", ((L,), (L,)))
+    out_f, _ = DeviceRun(full).step()
+    second = make_batch("mixed", lengths=([L - c], [L]))
+    second.q = full.q[c:].copy()
+    second.k, second.v = full.k, full.v
+    out_2, _ = DeviceRun(second).step()
+    first = make_batch("mixed", lengths=([c], [c]))
+    first.q = full.q[:c].copy()
+    first.k, first.v = full.k[:c].copy(), full.v[:c].copy()
+    out_1, _ = DeviceRun(first).step()
+    got = np.concatenate([out_1, out_2])
+    O, _ = oracle_outputs(full)
+    assert np.abs(got - O).max() <= tolerance(full)
+    assert np.abs(got - out_f).max() <= 2 * tolerance(full)

@@ -1,0 +1,231 @@
+"""C-ABI boundary on the CPU: the library loads, exports every entry point the
+header declares, rejects bad input with the documented status before doing
+any device work, and the planner's work list covers the batch exactly."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_attention_kv_pd_amd as pd
+from workloads import make_batch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pd_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pd_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "pd_plan" in names and "pd_kv_unpack" in names
+    for n in names:
+        assert hasattr(pd._lib, n), n
+    assert set(names) == set(pd.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in pd.version()
+    assert pd._lib.pd_status_string(0) == b"PD_OK"
+    assert pd._lib.pd_status_string(-3) == b"PD_ERR_OUT_OF_RANGE"
+
+
+def desc(**kw):
+    base = dict(num_qo_heads=4, num_kv_heads=2, head_dim=64, page_size=16, dtype="f32")
+    base.update(kw)
+    return pd.make_desc(**base)
+
+
+def plan_args(qo=(3, 1), kv=(20, 17), ps=16, pool=10):
+    qo, kv = list(qo), list(kv)
+    npg = [(k + ps - 1) // ps for k in kv]
+    indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    ids = np.arange(indptr[-1], dtype=np.int32)
+    return qo, kv, indptr, ids, pool
+
+
+def expect(status, fn, *a, **kw):
+    with pytest.raises(pd.PdError) as e:
+        fn(*a, **kw)
+    assert e.value.name == status, str(e.value)
+    assert len(pd._lib.pd_last_error()) > 0
+
+
+def test_plan_accepts_valid_batch():
+    qo, kv, ip, ids, pool = plan_args()
+    p = pd.pd_plan(desc(), qo, kv, ip, ids, pool)
+    s = p.stats()
+    assert s.total_q_rows == 4 and s.batch == 2
+    assert p.workspace_bytes > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_kv_heads=3), "PD_ERR_INVALID_ARG"),     # 4 % 3 != 0
+    (dict(head_dim=96), "PD_ERR_UNSUPPORTED"),
+    (dict(page_size=8), "PD_ERR_UNSUPPORTED"),
+    (dict(dtype=7), "PD_ERR_UNSUPPORTED"),
+    (dict(num_qo_heads=0), "PD_ERR_INVALID_ARG"),
+    (dict(num_qo_heads=256, num_kv_heads=1), "PD_ERR_UNSUPPORTED"),
+])
+def test_plan_rejects_bad_desc(kw, status):
+    qo, kv, ip, ids, pool = plan_args()
+    expect(status, pd.pd_plan, desc(**kw), qo, kv, ip, ids, pool)
+
+
+def test_plan_rejects_bad_batches():
+    qo, kv, ip, ids, pool = plan_args()
+    d = desc()
+    expect("PD_ERR_INVALID_ARG", pd.pd_plan, d, [21, 1], kv, ip, ids, pool)        # qo > kv
+    expect("PD_ERR_INVALID_ARG", pd.pd_plan, d, [-1, 1], kv, ip, ids, pool)        # negative
+    expect("PD_ERR_INVALID_ARG", pd.pd_plan, d, qo, [20, 33], ip, ids, pool)       # page count
+    bad = ids.copy(); bad[2] = bad[0]
+    expect("PD_ERR_INVALID_ARG", pd.pd_plan, d, qo, kv, ip, bad, pool)             # duplicate page
+    bad = ids.copy(); bad[1] = pool
+    expect("PD_ERR_OUT_OF_RANGE", pd.pd_plan, d, qo, kv, ip, bad, pool)            # outside pool
+    bad = ids.copy(); bad[1] = -5
+    expect("PD_ERR_OUT_OF_RANGE", pd.pd_plan, d, qo, kv, ip, bad, pool)
+    expect("PD_ERR_INVALID_ARG", pd.pd_plan, d, [], [], [0], [], pool)             # empty batch
+    ip2 = ip.copy(); ip2[0] = 1
+    expect("PD_ERR_INVALID_ARG", pd.pd_plan, d, qo, kv, ip2, ids, pool)
+
+
+def test_plan_allows_empty_and_no_op_requests():
+    d = desc()
+    p = pd.pd_plan(d, [0, 0, 1], [0, 5, 1], [0, 0, 1, 2], [3, 4], 5)
+    s = p.stats()
+    assert s.total_q_rows == 1 and s.decode_row_groups == 2
+
+
+class FakeTensor:
+    """Host stand-in with a device-looking pointer: only for calls that must
+    fail in argument checking before any device work."""
+
+    def __init__(self, nbytes, ptr=0x1000):
+        self._n, self._p = nbytes, ptr
+        self.is_cuda = True
+
+    def is_contiguous(self):
+        return True
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return 1
+
+    def data_ptr(self):
+        return self._p
+
+
+def test_pack_unpack_reject_bad_lists_before_device_work():
+    d = desc()
+    pb = pd.pd_kv_pack_bytes(d, 1)
+    pool, buf, scr = FakeTensor(10 * pb), FakeTensor(2 * pb), FakeTensor(8)
+    for fn in (pd.pd_kv_pack, pd.pd_kv_unpack):
+        expect("PD_ERR_OUT_OF_RANGE", fn, d, pool, 10, [0, 10], buf, scr, stream=0)
+        expect("PD_ERR_INVALID_ARG", fn, d, pool, 10, [3, 3], buf, scr, stream=0)
+        expect("PD_ERR_WORKSPACE", fn, d, pool, 10, [1, 2, 3], FakeTensor(3 * pb), scr, stream=0)
+        expect("PD_ERR_WORKSPACE", fn, d, pool, 10, [1, 2], FakeTensor(pb), scr, stream=0)
+        expect("PD_ERR_UNSUPPORTED", fn, desc(head_dim=80), pool, 10, [1], buf, scr, stream=0)
+
+
+def test_upload_rejects_small_workspace():
+    qo, kv, ip, ids, pool = plan_args()
+    p = pd.pd_plan(desc(), qo, kv, ip, ids, pool)
+    expect("PD_ERR_WORKSPACE", pd.pd_plan_upload, p, FakeTensor(p.workspace_bytes - 1), stream=0)
+
+
+def test_pack_bytes_formula():
+    assert pd.pd_kv_pack_bytes(desc(), 7) == 7 * 2 * 2 * 16 * 64 * 4
+    assert pd.pd_kv_pack_bytes(desc(num_qo_heads=64, num_kv_heads=8, head_dim=128, page_size=64,
+                                    dtype="bf16"), 512) == 128 * 2 ** 20
+    assert pd.pd_kv_pack_bytes(desc(), -1) == 0
+
+
+# ------------------------------------------------------------- planner cover
+def check_cover(b, plan):
+    """Every (request, query head, row) is computed exactly once, prefill
+    tiles see exactly their causal key range, decode chunks tile [0, kv)."""
+    g = b.H_q // b.H_kv
+    pf, du, mg = plan.work_items(0), plan.work_items(1), plan.work_items(2)
+    seen = {}
+    for (r, hk, q0, nq, kv_end, *_rest) in pf:
+        qo, kv = int(b.qo_lens[r]), int(b.kv_lens[r])
+        assert qo * g > 16
+        assert nq * g <= 128 and 0 <= q0 and q0 + nq <= qo
+        assert kv_end == (kv - qo + q0 + nq if b.causal else kv)
+        for t in range(q0, q0 + nq):
+            for h in range(hk * g, hk * g + g):
+                seen[(r, h, t)] = seen.get((r, h, t), 0) + 1
+    parts = {}
+    for (r, hk, k0, k1, part, *_rest) in du:
+        assert k0 % 32 == 0 and k0 < k1 <= int(b.kv_lens[r])
+        parts[part] = (r, hk, k0, k1)
+    assert sorted(parts) == list(range(len(du)))
+    for (r, hk, p0, n) in mg:
+        qo, kv = int(b.qo_lens[r]), int(b.kv_lens[r])
+        assert qo * g <= 16
+        chunks = sorted(parts[p][2:] for p in range(p0, p0 + n))
+        assert all(parts[p][:2] == (r, hk) for p in range(p0, p0 + n))
+        assert chunks[0][0] == 0 and chunks[-1][1] == kv
+        assert all(chunks[i][1] == chunks[i + 1][0] for i in range(n - 1))
+        for t in range(qo):
+            for h in range(hk * g, hk * g + g):
+                seen[(r, h, t)] = seen.get((r, h, t), 0) + 1
+    expect_keys = {(r, h, t) for r in range(b.B) for h in range(b.H_q) for t in range(int(b.qo_lens[r]))}
+    assert set(seen) == expect_keys
+    assert all(v == 1 for v in seen.values())
+
+
+@pytest.mark.parametrize("wid,kw", [
+    ("tiny", {}),
+    ("decode", {}),
+    ("prefill", {}),
+    ("mixed", {}),
+    ("long", {}),
+    ("mixed", dict(lengths=([1, 5, 2, 300, 0, 17], [1, 100, 64, 300, 9, 1000]))),
+    ("tiny", dict(lengths=([4, 16, 1], [4, 40, 1]), heads=(8, 2))),
+    ("tiny", dict(lengths=([33, 3], [33, 70]), causal=False)),
+    ("long", dict(lengths=([1, 3, 9], [5000, 64, 9]), heads=(24, 8))),
+])
+def test_planner_covers_batch(wid, kw):
+    b = make_batch(wid, materialize=False, **kw)
+    d = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype, b.causal)
+    plan = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages)
+    check_cover(b, plan)
+    for chunk in (32, 100, 4096):
+        plan = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages,
+                          decode_chunk_keys=chunk)
+        check_cover(b, plan)
+
+
+def test_planner_work_figures_match_closed_forms():
+    """prefill flops = 4 D H_q x visible pairs; decode bytes = K + V read."""
+    for wid, flops, dbytes in [("tiny", 713_728, 40_960), ("prefill", 21_516_779_520, 0)]:
+        b = make_batch(wid, materialize=False)
+        d = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype)
+        s = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages).stats()
+        pairs = sum(q * (k - q) + q * (q + 1) // 2 for q, k in zip(b.qo_lens.tolist(), b.kv_lens.tolist())
+                    if q * (b.H_q // b.H_kv) > 16)
+        assert s.prefill_flops == 4 * b.D * b.H_q * pairs
+        assert s.prefill_flops == flops and s.decode_kv_bytes == dbytes
+    b = make_batch("long", materialize=False)
+    d = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype)
+    s = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages).stats()
+    assert s.prefill_flops == 7_696_715_612_160
+    assert s.decode_kv_bytes == 256 * 32768 * 2 * 8 * 128 * 2
+
+
+def test_prefill_tiles_of_a_group_share_an_xcd():
+    b = make_batch("long", materialize=False)
+    d = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype)
+    pf = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages).work_items(0)
+    xcd_of_head = {}
+    for i, row in enumerate(pf):
+        xcd_of_head.setdefault(int(row[1]), set()).add(i % 8)
+    assert all(len(v) == 1 for v in xcd_of_head.values())
+    assert len({next(iter(v)) for v in xcd_of_head.values()}) == 8
