@@ -88,6 +88,25 @@ def algorithmic_work(b, elt=2):
                 append_bytes=append_bytes)
 
 
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed PMC summary
+    (FETCH_SIZE and WRITE_SIZE runs, calibrated on the pack kernel's known
+    copy size), or None when the kernel source changed since the counters
+    were taken (the summary records the source hash)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attention_long_pmc_traffic.txt")
+    src = os.path.join(ROOT, "decode_attention_kv_pd_amd", "csrc", "kernels.hip")
+    if workload != "long" or not os.path.exists(path):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for line in open(path):
+        if line.startswith("TRAFFIC "):
+            kv = dict(t.split("=", 1) for t in line.split()[1:])
+            if kv.get("kernels_sha256_16") == digest:
+                return int(kv["bytes_per_launch"])
+    return None
+
+
 def cpu_baseline(b, n_dec, n_tok):
     """Time the float64 oracle on a bounded sample of the workload: n_dec
     decode requests (all heads, full 32768-token cache) and n_tok tokens of
@@ -239,7 +258,7 @@ def main():
                    "batch": b.B, "q_rows": n_rows, "pool_pages": b.num_pool_pages,
                    "pool_GB": round(b.num_pool_pages * b.page_bytes / 1e9, 2)},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.workload),
                      "kernel": "pd_attention_run (attn_bf16_kernel + merge_kernel)",
                      "algorithmic_bytes": attn_bytes, "algorithmic_flops": work["prefill_flops"],
                      "mfma_frac": round(work["prefill_flops"] / (t_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
