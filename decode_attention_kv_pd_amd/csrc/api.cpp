@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -79,10 +80,63 @@ struct pd_plan_s {
   size_t meta_bytes = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   int64_t prefill_flops = 0, decode_bytes = 0;
   std::vector<char> blob;  // host image of the workspace tables
-  void* pinned = nullptr;
-  hipEvent_t ev = nullptr;
-  bool ev_recorded = false;
 };
+
+namespace {
+
+// Pinned host staging for workspace uploads, shared by all plans and reused
+// across steps: a block is handed out again once the copy that last read it
+// has completed (its event), so re-planning every step allocates no pinned
+// memory in steady state.
+struct StagingBlock {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  hipEvent_t ev = nullptr;
+  bool recorded = false;
+};
+std::mutex g_staging_mu;
+std::vector<StagingBlock> g_staging;
+
+pd_status hip_fail(hipError_t e, const char* what);
+
+// Copies `n` bytes of `src` into a free pinned block and enqueues the
+// host-to-device copy on `stream`.
+pd_status staged_upload(void* dst, const void* src, size_t n, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_staging_mu);
+  StagingBlock* blk = nullptr;
+  for (auto& b : g_staging) {
+    if (b.bytes < n) continue;
+    if (b.recorded) {
+      hipError_t q = hipEventQuery(b.ev);
+      if (q == hipErrorNotReady) continue;
+      if (q != hipSuccess) return hip_fail(q, "staging event query");
+    }
+    blk = &b;
+    break;
+  }
+  if (!blk) {
+    StagingBlock b;
+    b.bytes = std::max<size_t>(n, 1 << 20);
+    hipError_t e = hipHostMalloc(&b.ptr, b.bytes, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "pinned staging allocation");
+    e = hipEventCreateWithFlags(&b.ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipHostFree(b.ptr);
+      return hip_fail(e, "staging event creation");
+    }
+    g_staging.push_back(b);
+    blk = &g_staging.back();
+  }
+  std::memcpy(blk->ptr, src, n);
+  hipError_t e = hipMemcpyAsync(dst, blk->ptr, n, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "workspace upload");
+  e = hipEventRecord(blk->ev, stream);
+  if (e != hipSuccess) return hip_fail(e, "staging event record");
+  blk->recorded = true;
+  return PD_OK;
+}
+
+}  // namespace
 
 namespace {
 
@@ -411,41 +465,13 @@ pd_status pd_plan_upload(pd_plan_t plan, void* d_ws, size_t ws_bytes, void* stre
     if (ws_bytes < plan->ws_bytes)
       return fail(PD_ERR_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, plan needs " +
                                         std::to_string(plan->ws_bytes));
-    hipError_t e;
-    if (!plan->pinned) {
-      e = hipHostMalloc(&plan->pinned, std::max<size_t>(plan->meta_bytes, kAlign), hipHostMallocDefault);
-      if (e != hipSuccess) {
-        plan->pinned = nullptr;
-        return hip_fail(e, "pinned staging allocation");
-      }
-      e = hipEventCreateWithFlags(&plan->ev, hipEventDisableTiming);
-      if (e != hipSuccess) return hip_fail(e, "event creation");
-    } else if (plan->ev_recorded) {
-      e = hipEventSynchronize(plan->ev);  // the previous upload still reads the staging buffer
-      if (e != hipSuccess) return hip_fail(e, "waiting for the previous upload");
-    }
-    std::memcpy(plan->pinned, plan->blob.data(), plan->meta_bytes);
-    hipStream_t st = (hipStream_t)stream;
-    e = hipMemcpyAsync(d_ws, plan->pinned, plan->meta_bytes, hipMemcpyHostToDevice, st);
-    if (e != hipSuccess) return hip_fail(e, "workspace upload");
-    e = hipEventRecord(plan->ev, st);
-    if (e != hipSuccess) return hip_fail(e, "event record");
-    plan->ev_recorded = true;
-    return PD_OK;
+    return staged_upload(d_ws, plan->blob.data(), plan->meta_bytes, (hipStream_t)stream);
   } catch (...) {
     return fail(PD_ERR_HIP, "unexpected error in upload");
   }
 }
 
-void pd_plan_free(pd_plan_t plan) {
-  if (!plan) return;
-  if (plan->ev) {
-    if (plan->ev_recorded) (void)hipEventSynchronize(plan->ev);
-    (void)hipEventDestroy(plan->ev);
-  }
-  if (plan->pinned) (void)hipHostFree(plan->pinned);
-  delete plan;
-}
+void pd_plan_free(pd_plan_t plan) { delete plan; }
 
 pd_status pd_kv_append(pd_plan_t plan, void* d_ws, void* kv_pool, const void* k_new, const void* v_new,
                        void* stream) {

@@ -34,6 +34,21 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Read-only planner tables (work items, request rows, page table) are read
+// through the constant address space, so wave-uniform reads become scalar
+// loads instead of vector loads followed by a full vmcnt wait.
+#define CONST_AS __attribute__((address_space(4)))
+template <class T>
+__device__ __forceinline__ T ldc(const T* p) {
+  static_assert(sizeof(T) % 4 == 0, "dword-sized tables");
+  T out;
+  const CONST_AS int32_t* src = (const CONST_AS int32_t*)p;
+  int32_t* dst = (int32_t*)&out;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) dst[i] = src[i];
+  return out;
+}
+
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -49,17 +64,19 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// 4 x 16 transposed LDS read: in each 16-lane group, lane j addresses row j/4,
-// columns 4*(j%4)..+3 of a 4-row block of 16-bit elements and receives column
+// Transposed LDS read of 16-bit elements: in each 16-lane group, lane j
+// addresses row j/4, columns 4*(j%4)..+3 of a 4-row block and receives column
 // j of that block (rows 0..3), two elements per dword.
-__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+__device__ __forceinline__ u32x2 lds_read_tr16(const LDS_AS char* p) {
   bf16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
   return __builtin_bit_cast(u32x2, t);
 }
 
+__device__ __forceinline__ u32x4 lds_read16(const LDS_AS char* p) { return *(const LDS_AS u32x4*)p; }
+
 // 16 bytes per lane, global -> LDS without passing through VGPRs.  `lds` is
 // the wave-uniform base of a 1 KiB destination; lane i lands at lds + 16 * i.
-__device__ __forceinline__ void load_lds16(const void* src, char* lds) {
+__device__ __forceinline__ void load_lds16(const void* src, LDS_AS char* lds) {
   __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)lds, 16, 0, 0);
 }
 
@@ -82,113 +99,169 @@ __device__ __forceinline__ float sum_x16(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
-// LDS swizzles (16-byte chunks within a row of D bf16 elements).
-// K rows are read 16 bytes per lane, eight consecutive rows per LDS cycle:
-// XOR with row % 8 spreads them over eight chunk positions.
-__device__ __forceinline__ int swz_k(int row) { return row & 7; }
-// V rows are read by the 4 x 16 transposed read (4 rows x 32 bytes per
-// 16-lane group): XOR with 2 * (row % 4) keeps each 32-byte pair together and
-// moves the four rows to four different pairs.
-__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 1; }
+// Softmax scaling is kept against a reference maximum that is only raised
+// when a row's running maximum exceeds it by more than 2^kRescaleLog2 in the
+// exp2 domain: P values stay <= 2^kRescaleLog2 (exact in fp32, 8-bit
+// mantissa in bf16 either way) and the O rescale is skipped on most tiles.
+// Output = sum(p v) / sum(p) is independent of the reference chosen.
+constexpr float kRescaleLog2 = 8.f;
+
+// LDS tile layout (K and V tiles of the prefill role, V stages of the decode
+// role): rows of D bf16 go into 1 KiB load blocks of RPB = 512 / D rows; in a
+// block the 16-byte chunks are stored chunk-major (slot = chunk * RPB + row)
+// and blocks are 1088 bytes apart (64 bytes of padding).  One direct
+// global->LDS load fills one block (lane l takes chunk l / RPB of row l % RPB,
+// so each load still reads RPB whole rows from HBM).  With this layout the K
+// reads (16 bytes per lane, consecutive rows on consecutive lanes) and the
+// transposed V reads (4 rows x 32 bytes per 16 lanes) touch distinct banks,
+// and every read address is a per-lane constant plus an immediate.
+template <int D>
+struct Lds {
+  static constexpr int RPB = 512 / D;
+  static constexpr int BLOCK = 1088;
+  static constexpr int ROW_BYTES = 2 * D;
+  __device__ static constexpr int off(int row, int chunk) {
+    return (row / RPB) * BLOCK + 16 * (chunk * RPB + row % RPB);
+  }
+  static constexpr int bytes(int rows) { return rows / RPB * BLOCK; }
+};
+
+// Byte offset of (page, kv half, head) in the pool.
+__device__ __forceinline__ int64_t page_head_off(const AttnParams& p, int page, int half, int hk) {
+  return ((int64_t)page * p.page_elems + (int64_t)(half * p.H_kv + hk) * p.ps * p.D) * 2;
+}
 
 // ------------------------------------------------------------------------
 // Decode role: one wavefront computes one DecodeItem (<= 16 query rows of
 // one KV head over keys [k0, k1)), 32 keys per step.
-//   S^T[key][col] = K Q^T on v_mfma_f32_16x16x32_bf16 (K from global straight
+//   S^T[key][col] = K Q^T on v_mfma_f32_16x16x32_bf16 (K from HBM straight
 //   into the A operand; Q^T held in registers as the B operand);
 //   online softmax per column across the four 16-lane groups;
-//   O^T[d][col] += V^T P^T on the same MFMA, V staged through LDS by direct
-//   global->LDS loads and read back transposed; P^T comes from the S
-//   accumulators without any lane exchange (key order inside the 32-key step
-//   is permuted identically in both operands).
+//   O^T[d][col] += V^T P^T on the same MFMA, V staged through a per-wave LDS
+//   double buffer by direct global->LDS loads and read back transposed; P^T
+//   comes from the S accumulators without any lane exchange (key order inside
+//   the 32-key step is permuted identically in both operands).
 // ------------------------------------------------------------------------
 template <int D>
 struct DecodeCfg {
   static constexpr int KS = D / 32;               // 32-wide k-steps of S
   static constexpr int DB = D / 16;               // 16-row d-blocks of O^T
-  static constexpr int ROW_BYTES = 2 * D;
-  static constexpr int CPR = D / 8;               // 16-byte chunks per row
-  static constexpr int RPI = 64 / CPR;            // rows per 1 KiB load
-  static constexpr int VLOADS = 32 / RPI;         // V loads per 32-key step
-  static constexpr int STAGE_BYTES = 32 * ROW_BYTES;
+  static constexpr int RPB = Lds<D>::RPB;
+  static constexpr int VLOADS = 32 / RPB;         // V loads per 32-key step
+  static constexpr int STAGE_BYTES = Lds<D>::bytes(32);
   static constexpr int WAVE_LDS = 2 * STAGE_BYTES;
 };
 
-template <int D>
-__device__ __forceinline__ void decode_issue(const AttnParams& p, const ReqInfo& ri, int hk, int b,
-                                             int lane, u32x4 (&kf)[2][D / 32], char* stage) {
-  using C = DecodeCfg<D>;
-  const uint16_t* pool = (const uint16_t*)p.pool;
+// Page ids of the two 16-key groups of the 32-key step at key b (clamped to
+// the request's last key, so a step past the end reads the last page).
+__device__ __forceinline__ int2 decode_pages(const AttnParams& p, const ReqInfo& ri, int b) {
   const int32_t* pages = p.page_indices + ri.page_start;
   const int kvm1 = ri.kv - 1;
+  return make_int2(ldc(pages + min(b, kvm1) / p.ps), ldc(pages + min(b + 16, kvm1) / p.ps));
+}
+
+// Loads of one 32-key step at key b: K fragments into `kf`, V rows into the
+// LDS stage.  Keys >= kv (only in the request's last step) are read from row
+// kv - 1 instead (finite data, masked later), so tail slots are never read.
+template <int D>
+__device__ __forceinline__ void decode_issue(const AttnParams& p, const ReqInfo& ri, int hk, int b, int2 pg,
+                                             int lane, u32x4 (&kf)[2][D / 32], LDS_AS char* stage) {
+  using C = DecodeCfg<D>;
+  const char* pool = (const char*)p.pool;
   const int psm = p.ps - 1;
   const int n = lane & 15, q = lane >> 4;
-  int64_t kbase[2], vbase[2];
+  const int kvm1 = ri.kv - 1;
+  const int r = lane % C::RPB, c = lane / C::RPB;
+  if (b + 32 <= ri.kv) {
+    // every row valid: uniform page bases, loop-invariant lane offsets
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    const int j0 = b + 16 * sb;
-    const int page = pages[min(j0, kvm1) / p.ps];  // wave-uniform
-    kbase[sb] = (int64_t)page * p.page_elems + (int64_t)hk * p.ps * D;
-    vbase[sb] = (int64_t)page * p.page_elems + (int64_t)(p.H_kv + hk) * p.ps * D;
-    const int row = min(j0 + n, kvm1) & psm;
-    const uint16_t* kp = pool + kbase[sb] + (int64_t)row * D + 8 * q;
+    for (int sb = 0; sb < 2; ++sb) {
+      const int j0 = b + 16 * sb;
+      const int page = sb ? pg.y : pg.x;
+      const int slot0 = j0 & psm;
+      const char* kb = pool + page_head_off(p, page, 0, hk) + slot0 * 2 * D;
+      const char* vb = pool + page_head_off(p, page, 1, hk) + slot0 * 2 * D;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) kf[sb][ks] = *(const u32x4*)(kp + 32 * ks);
-  }
+      for (int ks = 0; ks < C::KS; ++ks) kf[sb][ks] = *(const u32x4*)(kb + n * 2 * D + 16 * q + 64 * ks);
 #pragma unroll
-  for (int i = 0; i < C::VLOADS; ++i) {
-    const int R = i * C::RPI + lane / C::CPR;  // row of the 32-key step
-    const int pc = lane % C::CPR;
-    const int c = pc ^ swz_v(R);
-    const int sb = (i * C::RPI) >> 4;
-    const int row = min(b + R, kvm1) & psm;
-    const uint16_t* vp = pool + vbase[sb] + (int64_t)row * D + 8 * c;
-    load_lds16(vp, stage + i * 1024);
+      for (int i = 0; i < C::VLOADS / 2; ++i)
+        load_lds16(vb + (i * C::RPB + r) * 2 * D + 16 * c,
+                   stage + (sb * (C::VLOADS / 2) + i) * Lds<D>::BLOCK);
+    }
+  } else {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int j0 = b + 16 * sb;
+      const int page = sb ? pg.y : pg.x;
+      const char* kb = pool + page_head_off(p, page, 0, hk);
+      const char* vb = pool + page_head_off(p, page, 1, hk);
+      const int krow = min(j0 + n, kvm1) & psm;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) kf[sb][ks] = *(const u32x4*)(kb + krow * 2 * D + 16 * q + 64 * ks);
+#pragma unroll
+      for (int i = 0; i < C::VLOADS / 2; ++i) {
+        const int vrow = min(j0 + i * C::RPB + r, kvm1) & psm;
+        load_lds16(vb + vrow * 2 * D + 16 * c, stage + (sb * (C::VLOADS / 2) + i) * Lds<D>::BLOCK);
+      }
+    }
   }
 }
+
+struct DecodeLanes {
+  int q;         // 16-lane group
+  int v_off;     // lane part of the transposed V read address
+};
 
 // One 32-key step of a decode unit: issue the next step's loads (K into
 // `kn`, V into LDS stage `sn`), wait for this step's, then S, softmax, PV.
 template <int D>
 __device__ __forceinline__ void decode_step(const AttnParams& p, const ReqInfo& ri, int hk, int b, int k1,
-                                            int lim, int lane, const u32x4 (&qf)[D / 32],
-                                            const u32x4 (&kc)[2][D / 32], u32x4 (&kn)[2][D / 32],
-                                            const char* st, char* sn, float& m_run, float& l_run,
+                                            int lim, int mask_from, DecodeLanes ln, int lane,
+                                            const u32x4 (&qf)[D / 32], const u32x4 (&kc)[2][D / 32],
+                                            u32x4 (&kn)[2][D / 32], const LDS_AS char* st, LDS_AS char* sn,
+                                            int2& pg_next, float& m_ref, float& l_run,
                                             f32x4 (&oacc)[D / 16]) {
   using C = DecodeCfg<D>;
-  const int q = lane >> 4;
   const float cl = p.c_log2;
   const int nb = b + 32;
   if (nb < k1) {
-    decode_issue<D>(p, ri, hk, nb, lane, kn, sn);
+    const int2 pg = pg_next;
+    if (nb + 32 < k1) pg_next = decode_pages(p, ri, nb + 32);  // scalar loads, used next step
+    decode_issue<D>(p, ri, hk, nb, pg, lane, kn, sn);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::KS + C::VLOADS) : "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  // S^T for keys b + 16 sb + 4 q + i, column n
+  // S^T for keys b + 16 sb + 4 q + i, column lane & 15
   f32x4 s[2];
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
-    s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s[sb] = mfma16(kc[sb][0], qf[0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) s[sb] = mfma16(kc[sb][ks], qf[ks], s[sb]);
+    for (int ks = 1; ks < C::KS; ++ks) s[sb] = mfma16(kc[sb][ks], qf[ks], s[sb]);
   }
-  float mx = -INFINITY;
+  if (b + 32 > mask_from) {
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = b + 16 * sb + 4 * q + i;
-      if (key >= lim) s[sb][i] = -INFINITY;
-      mx = fmaxf(mx, s[sb][i]);
-    }
+      for (int i = 0; i < 4; ++i)
+        if (b + 16 * sb + 4 * ln.q + i >= lim) s[sb][i] = -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
   mx = max_x16(mx);
   mx = max_x32(mx);
-  const float m_new = fmaxf(m_run, mx);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = fast_exp2((m_run - m_use) * cl);
-  const float mc = m_use * cl;
+  if (wave_any(mx * cl > m_ref * cl + kRescaleLog2)) {
+    const float m_new = fmaxf(m_ref, mx);
+    const float alpha = fast_exp2((m_ref - m_new) * cl);  // m_ref = -inf -> 0
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) oacc[db] = oacc[db] * alpha;
+    m_ref = m_new;
+  }
+  const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * cl;
   float psum = 0.f;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
@@ -197,32 +270,26 @@ __device__ __forceinline__ void decode_step(const AttnParams& p, const ReqInfo& 
       s[sb][i] = fast_exp2(__builtin_fmaf(s[sb][i], cl, -mc));
       psum += s[sb][i];
     }
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-  u32x4 pb = {pack_bf16(s[0][0], s[0][1]), pack_bf16(s[0][2], s[0][3]),
-              pack_bf16(s[1][0], s[1][1]), pack_bf16(s[1][2], s[1][3])};
-  // V^T[d = 16 db + j][keys 4q + e, 16 + 4q + e] from the transposed read
-  const int j = lane & 15;
-  const int r1 = 4 * q + (j >> 2);
-  const int r2 = r1 + 16;
-  const int half = (j & 1) * 8;
+  l_run += psum;
+  const u32x4 pb = {pack_bf16(s[0][0], s[0][1]), pack_bf16(s[0][2], s[0][3]),
+                    pack_bf16(s[1][0], s[1][1]), pack_bf16(s[1][2], s[1][3])};
+  // V^T[d = 16 db + (lane & 15)][keys 4q + e, 16 + 4q + e]
+  const LDS_AS char* vp = st + ln.v_off;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
-    const int c = 2 * db + ((j & 3) >> 1);
-    u32x2 a1 = lds_read_tr16(st + r1 * C::ROW_BYTES + ((c ^ swz_v(r1)) << 4) + half);
-    u32x2 a2 = lds_read_tr16(st + r2 * C::ROW_BYTES + ((c ^ swz_v(r2)) << 4) + half);
-    u32x4 a = {a1[0], a1[1], a2[0], a2[1]};
-    oacc[db] = oacc[db] * alpha;
+    const u32x2 a1 = lds_read_tr16(vp + 32 * C::RPB * db);
+    const u32x2 a2 = lds_read_tr16(vp + 32 * C::RPB * db + (16 / C::RPB) * Lds<D>::BLOCK);
+    const u32x4 a = {a1[0], a1[1], a2[0], a2[1]};
     oacc[db] = mfma16(a, pb, oacc[db]);
   }
 }
 
 template <int D>
-__device__ void decode_unit(const AttnParams& p, int unit, char* lds) {
+__device__ void decode_unit(const AttnParams& p, int unit, LDS_AS char* lds) {
   using C = DecodeCfg<D>;
   const int lane = threadIdx.x & 63;
-  const DecodeItem it = p.du[unit];
-  const ReqInfo ri = p.req[it.req];
+  const DecodeItem it = ldc(p.du + unit);
+  const ReqInfo ri = ldc(p.req + it.req);
   const int g = p.g;
   const int nrows = ri.qo * g;
   const int n = lane & 15, q = lane >> 4;
@@ -230,13 +297,20 @@ __device__ void decode_unit(const AttnParams& p, int unit, char* lds) {
   const int t = col_ok ? n / g : 0;
   const int h = it.hk * g + (col_ok ? n % g : 0);
   const int lim = min(it.k1, p.causal ? ri.kv - ri.qo + t + 1 : ri.kv);
+  const int mask_from = min(it.k1, p.causal ? ri.kv - ri.qo + 1 : ri.kv);  // smallest lim of any column
+  DecodeLanes ln;
+  ln.q = q;
+  {
+    const int j = lane & 15;
+    ln.v_off = Lds<D>::off(4 * q + (j >> 2), (j & 3) >> 1) + 8 * (j & 1);
+  }
 
   u32x4 qf[C::KS];
   {
     const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)(ri.qo_start + t) * p.H_q + h) * D + 8 * q;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 v = *(const u32x4*)(qp + 32 * ks);
+      const u32x4 v = *(const u32x4*)(qp + 32 * ks);
       qf[ks] = col_ok ? v : u32x4{0, 0, 0, 0};
     }
   }
@@ -244,16 +318,19 @@ __device__ void decode_unit(const AttnParams& p, int unit, char* lds) {
   f32x4 oacc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
 
   u32x4 kf0[2][C::KS], kf1[2][C::KS];
-  decode_issue<D>(p, ri, it.hk, it.k0, lane, kf0, lds);
+  LDS_AS char* st0 = lds;
+  LDS_AS char* st1 = lds + C::STAGE_BYTES;
+  int2 pg_next = decode_pages(p, ri, it.k0 + 32);
+  decode_issue<D>(p, ri, it.hk, it.k0, decode_pages(p, ri, it.k0), lane, kf0, st0);
   for (int b = it.k0;;) {
-    decode_step<D>(p, ri, it.hk, b, it.k1, lim, lane, qf, kf0, kf1, lds, lds + C::STAGE_BYTES, m_run,
+    decode_step<D>(p, ri, it.hk, b, it.k1, lim, mask_from, ln, lane, qf, kf0, kf1, st0, st1, pg_next, m_ref,
                    l_run, oacc);
     b += 32;
     if (b >= it.k1) break;
-    decode_step<D>(p, ri, it.hk, b, it.k1, lim, lane, qf, kf1, kf0, lds + C::STAGE_BYTES, lds, m_run,
+    decode_step<D>(p, ri, it.hk, b, it.k1, lim, mask_from, ln, lane, qf, kf1, kf0, st1, st0, pg_next, m_ref,
                    l_run, oacc);
     b += 32;
     if (b >= it.k1) break;
@@ -268,7 +345,7 @@ __device__ void decode_unit(const AttnParams& p, int unit, char* lds) {
     for (int db = 0; db < C::DB; ++db) *(f32x4*)(po + 16 * db) = oacc[db] * inv;
     if (q == 0)
       p.part_lse[(int64_t)it.part * kDecodeCols + n] =
-          l_tot > 0.f ? m_run * p.sm_scale + __logf(l_tot) : -INFINITY;
+          l_tot > 0.f ? m_ref * p.sm_scale + __logf(l_tot) : -INFINITY;
   }
 }
 
@@ -280,164 +357,225 @@ __device__ void decode_unit(const AttnParams& p, int unit, char* lds) {
 //   registers; K and V tiles are staged in LDS (double buffered, direct
 //   global->LDS loads, one 16-row page group per wave); K is read back 16
 //   bytes per lane, V with the transposed read; P^T is the S accumulator
-//   re-packed to bf16 in place.  Only tiles that cross the causal diagonal
-//   (or the end of the cache) are masked.
+//   re-packed to bf16 in place.  Tiles that cross the causal diagonal (or the
+//   end of the cache) run a separate masked copy of the loop body.
 // ------------------------------------------------------------------------
 template <int D>
 struct PrefillCfg {
   static constexpr int KS = D / 16;     // 16-wide k-steps of S
   static constexpr int DB = D / 32;     // 32-row d-blocks of O^T
-  static constexpr int ROW_BYTES = 2 * D;
-  static constexpr int CPR = D / 8;
-  static constexpr int RPI = 64 / CPR;  // rows per 1 KiB load
-  static constexpr int LOADS = 16 / RPI;
-  static constexpr int TILE_BYTES = 64 * ROW_BYTES;
+  static constexpr int RPB = Lds<D>::RPB;
+  static constexpr int LOADS = 16 / RPB;  // 1 KiB loads per wave per matrix per tile
+  static constexpr int TILE_BYTES = Lds<D>::bytes(64);
   static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K, V x 2 buffers
 };
 
-template <int D>
-__device__ __forceinline__ void prefill_issue(const AttnParams& p, const ReqInfo& ri, int hk,
-                                              int kv_end, int kbase, int w, int lane, char* kbuf,
-                                              char* vbuf) {
-  using C = PrefillCfg<D>;
-  const uint16_t* pool = (const uint16_t*)p.pool;
-  const int32_t* pages = p.page_indices + ri.page_start;
-  const int last = kv_end - 1;
-  const int j0 = kbase + 16 * w;
-  const int page = pages[min(j0, last) / p.ps];
-  const int64_t kb = (int64_t)page * p.page_elems + (int64_t)hk * p.ps * D;
-  const int64_t vb = (int64_t)page * p.page_elems + (int64_t)(p.H_kv + hk) * p.ps * D;
-  const int psm = p.ps - 1;
-#pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int R0 = 16 * w + i * C::RPI;
-    const int R = R0 + lane / C::CPR;
-    const int pc = lane % C::CPR;
-    const int row = min(kbase + R, last) & psm;
-    load_lds16(pool + kb + (int64_t)row * D + 8 * (pc ^ swz_k(R)), kbuf + R0 * C::ROW_BYTES);
-    load_lds16(pool + vb + (int64_t)row * D + 8 * (pc ^ swz_v(R)), vbuf + R0 * C::ROW_BYTES);
-  }
+// Loads of the 64-key tile at kbase (wave w: rows 16 w .. 16 w + 15, one page
+// group).  `full`: every row < kv_end; otherwise rows past kv_end - 1 are read
+// from row kv_end - 1 (finite, masked later).
+// Page id of wave w's 16-row group of the tile at kbase (clamped to the
+// tile's last key).
+__device__ __forceinline__ int prefill_page(const AttnParams& p, const ReqInfo& ri, int kv_end, int kbase,
+                                            int w) {
+  return ldc(p.page_indices + ri.page_start + min(kbase + 16 * w, kv_end - 1) / p.ps);
 }
 
 template <int D>
-__device__ void prefill_tile(const AttnParams& p, int item, char* lds) {
+__device__ __forceinline__ void prefill_issue(const AttnParams& p, int hk, int kv_end, int kbase, int w,
+                                              int page, int lane, bool full, LDS_AS char* kt,
+                                              LDS_AS char* vt) {
   using C = PrefillCfg<D>;
+  const char* pool = (const char*)p.pool;
+  const int psm = p.ps - 1;
+  const int r = lane % C::RPB, c = lane / C::RPB;
+  const int j0 = kbase + 16 * w;
+  LDS_AS char* kd = kt + (16 / C::RPB) * w * Lds<D>::BLOCK;
+  LDS_AS char* vd = vt + (16 / C::RPB) * w * Lds<D>::BLOCK;
+  if (full) {
+    const int slot0 = j0 & psm;
+    const char* kb = pool + page_head_off(p, page, 0, hk) + slot0 * 2 * D;
+    const char* vb = pool + page_head_off(p, page, 1, hk) + slot0 * 2 * D;
+    const int lo = r * 2 * D + 16 * c;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      load_lds16(kb + i * C::RPB * 2 * D + lo, kd + i * Lds<D>::BLOCK);
+      load_lds16(vb + i * C::RPB * 2 * D + lo, vd + i * Lds<D>::BLOCK);
+    }
+  } else {
+    const int last = kv_end - 1;
+    const char* kb = pool + page_head_off(p, page, 0, hk);
+    const char* vb = pool + page_head_off(p, page, 1, hk);
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int row = min(j0 + i * C::RPB + r, last) & psm;
+      load_lds16(kb + row * 2 * D + 16 * c, kd + i * Lds<D>::BLOCK);
+      load_lds16(vb + row * 2 * D + 16 * c, vd + i * Lds<D>::BLOCK);
+    }
+  }
+}
+
+struct PrefillLanes {
+  int h2;     // lane >> 5: which 4-key half of each 8-key group this lane holds
+  int k_off;  // lane part of the K read address
+  int v_off;  // lane part of the transposed V read address
+};
+
+// S, softmax and PV of one 64-key tile already in LDS.
+template <int D, bool MASK>
+__device__ __forceinline__ void prefill_compute(const AttnParams& p, const LDS_AS char* kt,
+                                                const LDS_AS char* vt, int kbase, int lim, PrefillLanes ln,
+                                                const u32x4 (&qf)[D / 16], float& m_ref, float& l_run,
+                                                f32x16 (&oacc)[D / 32]) {
+  using C = PrefillCfg<D>;
+  constexpr int RPB = C::RPB;
+  const float cl = p.c_log2;
+  // S^T[key 32 kb + 8 jj + 4 h2 + i][query] in s[kb][4 jj + i]; the two
+  // accumulator chains are interleaved and K is read one k-step ahead
+  f32x16 s[2];
+  const LDS_AS char* kp = kt + ln.k_off;
+  constexpr int KB1 = (32 / RPB) * Lds<D>::BLOCK;
+  u32x4 a0 = lds_read16(kp), a1 = lds_read16(kp + KB1);
+  u32x4 n0 = lds_read16(kp + 32 * RPB), n1 = lds_read16(kp + KB1 + 32 * RPB);
+  s[0] = mfma32(a0, qf[0], f32x16{});
+  s[1] = mfma32(a1, qf[0], f32x16{});
+#pragma unroll
+  for (int ks = 1; ks < C::KS; ++ks) {
+    a0 = n0;
+    a1 = n1;
+    if (ks + 1 < C::KS) {
+      n0 = lds_read16(kp + 32 * RPB * (ks + 1));
+      n1 = lds_read16(kp + KB1 + 32 * RPB * (ks + 1));
+    }
+    s[0] = mfma32(a0, qf[ks], s[0]);
+    s[1] = mfma32(a1, qf[ks], s[1]);
+  }
+  if (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kbase + 32 * kb + 8 * (r >> 2) + 4 * ln.h2 + (r & 3) >= lim) s[kb][r] = -INFINITY;
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+  mx = max_x32(mx);
+  if (wave_any(mx * cl > m_ref * cl + kRescaleLog2)) {
+    const float m_new = fmaxf(m_ref, mx);
+    const float alpha = fast_exp2((m_ref - m_new) * cl);  // m_ref = -inf -> 0
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) oacc[db] = oacc[db] * alpha;
+    m_ref = m_new;
+  }
+  const float mc = m_ref * cl;
+  float psum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], cl, -mc));
+      psum += s[kb][r];
+    }
+  l_run += psum;
+  // O^T += V^T P^T over the four 16-key k-steps
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+      const u32x4 pb = {pack_bf16(s[kb][8 * sp + 0], s[kb][8 * sp + 1]),
+                        pack_bf16(s[kb][8 * sp + 2], s[kb][8 * sp + 3]),
+                        pack_bf16(s[kb][8 * sp + 4], s[kb][8 * sp + 5]),
+                        pack_bf16(s[kb][8 * sp + 6], s[kb][8 * sp + 7])};
+      const LDS_AS char* vp = vt + ln.v_off + ((32 * kb + 16 * sp) / RPB) * Lds<D>::BLOCK;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const u32x2 a1 = lds_read_tr16(vp + 64 * RPB * db);
+        const u32x2 a2 = lds_read_tr16(vp + 64 * RPB * db + (8 / RPB) * Lds<D>::BLOCK);
+        const u32x4 a = {a1[0], a1[1], a2[0], a2[1]};
+        oacc[db] = mfma32(a, pb, oacc[db]);
+      }
+    }
+}
+
+template <int D>
+__device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
+  using C = PrefillCfg<D>;
+  constexpr int RPB = C::RPB;
   const int lane = threadIdx.x & 63;
   const int w = uniform_i(threadIdx.x >> 6);
-  const PrefillItem it = p.pf[item];
-  const ReqInfo ri = p.req[it.req];
+  const PrefillItem it = ldc(p.pf + item);
+  const ReqInfo ri = ldc(p.req + it.req);
   const int g = p.g;
   const int rows = it.nq * g;
   const int nloc = lane & 31;
-  const int h2 = lane >> 5;
   const int n = 32 * w + nloc;
   const bool row_ok = n < rows;
   const int t = row_ok ? n / g : 0;
   const int h = it.hk * g + (row_ok ? n % g : 0);
   const int qpos0 = ri.kv - ri.qo + it.q0;  // absolute position of the tile's first token
   const int lim = p.causal ? qpos0 + t + 1 : ri.kv;
-  const int tile_min_lim = p.causal ? qpos0 + 1 : it.kv_end;  // smallest limit of any row
+  const int mask_from = p.causal ? qpos0 + 1 : it.kv_end;  // smallest limit of any row
   const int64_t qrow = (int64_t)(ri.qo_start + it.q0 + t) * p.H_q + h;
+
+  PrefillLanes ln;
+  ln.h2 = lane >> 5;
+  ln.k_off = Lds<D>::off(nloc, ln.h2);
+  {
+    const int j = lane & 15, dhalf = (lane >> 4) & 1;
+    ln.v_off = Lds<D>::off(4 * ln.h2 + (j >> 2), 2 * dhalf + ((j & 3) >> 1)) + 8 * (j & 1);
+  }
 
   u32x4 qf[C::KS];
   {
-    const uint16_t* qp = (const uint16_t*)p.q + qrow * D + 8 * h2;
+    const uint16_t* qp = (const uint16_t*)p.q + qrow * D + 8 * ln.h2;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 v = *(const u32x4*)(qp + 16 * ks);
+      const u32x4 v = *(const u32x4*)(qp + 16 * ks);
       qf[ks] = row_ok ? v : u32x4{0, 0, 0, 0};
     }
   }
   f32x16 oacc[C::DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float cl = p.c_log2;
+  for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
+  float m_ref = -INFINITY, l_run = 0.f;
 
-  char* kbuf[2] = {lds, lds + C::TILE_BYTES};
-  char* vbuf[2] = {lds + 2 * C::TILE_BYTES, lds + 3 * C::TILE_BYTES};
+  LDS_AS char* kbuf = lds;
+  LDS_AS char* vbuf = lds + 2 * C::TILE_BYTES;
   const int ntiles = (it.kv_end + 63) >> 6;
-  prefill_issue<D>(p, ri, it.hk, it.kv_end, 0, w, lane, kbuf[0], vbuf[0]);
-  for (int kt = 0; kt < ntiles; ++kt) {
+  const int nfull = it.kv_end >> 6;                                  // tiles with every row < kv_end
+  const int nplain = min(ntiles, mask_from / 64);  // tiles whose keys all lie below every row's limit
+  int pg_next = prefill_page(p, ri, it.kv_end, 64, w);
+  prefill_issue<D>(p, it.hk, it.kv_end, 0, w, prefill_page(p, ri, it.kv_end, 0, w), lane, 0 < nfull, kbuf,
+                   vbuf);
+  int kt = 0;
+  for (; kt < nplain; ++kt) {
     const int buf = kt & 1;
-    const int kbase = kt * 64;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + 1 < ntiles)
-      prefill_issue<D>(p, ri, it.hk, it.kv_end, kbase + 64, w, lane, kbuf[buf ^ 1], vbuf[buf ^ 1]);
-    const char* kt_lds = kbuf[buf];
-    const char* vt_lds = vbuf[buf];
-    // S^T[key 32 kb + 8 jj + 4 h2 + i][query n] in s[kb][4 jj + i]
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int R = 32 * kb + nloc;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const int c = 2 * ks + h2;
-        u32x4 a = *(const u32x4*)(kt_lds + R * C::ROW_BYTES + ((c ^ swz_k(R)) << 4));
-        s[kb] = mfma32(a, qf[ks], s[kb]);
-      }
+    if (kt + 1 < ntiles) {
+      const int pg = pg_next;
+      if (kt + 2 < ntiles) pg_next = prefill_page(p, ri, it.kv_end, (kt + 2) * 64, w);
+      prefill_issue<D>(p, it.hk, it.kv_end, (kt + 1) * 64, w, pg, lane, kt + 1 < nfull,
+                       kbuf + (buf ^ 1) * C::TILE_BYTES, vbuf + (buf ^ 1) * C::TILE_BYTES);
     }
-    if (kbase + 64 > tile_min_lim) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + 32 * kb + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          if (key >= lim) s[kb][r] = -INFINITY;
-        }
+    prefill_compute<D, false>(p, kbuf + buf * C::TILE_BYTES, vbuf + buf * C::TILE_BYTES, kt * 64, lim, ln,
+                              qf, m_ref, l_run, oacc);
+  }
+  for (; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 1 < ntiles) {
+      const int pg = pg_next;
+      if (kt + 2 < ntiles) pg_next = prefill_page(p, ri, it.kv_end, (kt + 2) * 64, w);
+      prefill_issue<D>(p, it.hk, it.kv_end, (kt + 1) * 64, w, pg, lane, kt + 1 < nfull,
+                       kbuf + (buf ^ 1) * C::TILE_BYTES, vbuf + (buf ^ 1) * C::TILE_BYTES);
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_x32(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * cl);
-    const float mc = m_use * cl;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], cl, -mc));
-        psum += s[kb][r];
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) oacc[db] = oacc[db] * alpha;
-    // O^T += V^T P^T over the four 16-key k-steps
-    const int G = lane >> 4;
-    const int j = lane & 15;
-    const int dhalf = G & 1;
-    const int half = (j & 1) * 8;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp) {
-        u32x4 pb = {pack_bf16(s[kb][8 * sp + 0], s[kb][8 * sp + 1]),
-                    pack_bf16(s[kb][8 * sp + 2], s[kb][8 * sp + 3]),
-                    pack_bf16(s[kb][8 * sp + 4], s[kb][8 * sp + 5]),
-                    pack_bf16(s[kb][8 * sp + 6], s[kb][8 * sp + 7])};
-        const int r1 = 32 * kb + 16 * sp + 4 * h2 + (j >> 2);
-        const int r2 = r1 + 8;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const int c = 4 * db + 2 * dhalf + ((j & 3) >> 1);
-          u32x2 a1 = lds_read_tr16(vt_lds + r1 * C::ROW_BYTES + ((c ^ swz_v(r1)) << 4) + half);
-          u32x2 a2 = lds_read_tr16(vt_lds + r2 * C::ROW_BYTES + ((c ^ swz_v(r2)) << 4) + half);
-          u32x4 a = {a1[0], a1[1], a2[0], a2[1]};
-          oacc[db] = mfma32(a, pb, oacc[db]);
-        }
-      }
+    prefill_compute<D, true>(p, kbuf + buf * C::TILE_BYTES, vbuf + buf * C::TILE_BYTES, kt * 64, lim, ln,
+                             qf, m_ref, l_run, oacc);
   }
   const float l_tot = sum_x32(l_run);
   if (row_ok) {
@@ -447,10 +585,10 @@ __device__ void prefill_tile(const AttnParams& p, int item, char* lds) {
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        f32x4 v = {oacc[db][4 * jj + 0], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
-        *(f32x4*)(op + 32 * db + 8 * jj + 4 * h2) = v * inv;
+        const f32x4 v = {oacc[db][4 * jj + 0], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
+        *(f32x4*)(op + 32 * db + 8 * jj + 4 * ln.h2) = v * inv;
       }
-    if (h2 == 0 && p.lse) p.lse[qrow] = m_run * p.sm_scale + __logf(l_tot);
+    if (ln.h2 == 0 && p.lse) p.lse[qrow] = m_ref * p.sm_scale + __logf(l_tot);
   }
 }
 
@@ -458,8 +596,9 @@ __device__ void prefill_tile(const AttnParams& p, int item, char* lds) {
 // hold four decode units each (one per wavefront).
 template <int D>
 __global__ __launch_bounds__(kBlockThreads, 2) void attn_bf16_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[PrefillCfg<D>::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_raw[PrefillCfg<D>::LDS_BYTES];
   static_assert(kWavesPerBlock * DecodeCfg<D>::WAVE_LDS <= PrefillCfg<D>::LDS_BYTES, "lds");
+  LDS_AS char* lds = (LDS_AS char*)lds_raw;
   const int b = blockIdx.x;
   if (b < p.n_pf) {
     prefill_tile<D>(p, b, lds);
@@ -540,8 +679,8 @@ __global__ __launch_bounds__(kBlockThreads) void attn_f32_kernel(AttnParams p) {
   const int b = blockIdx.x;
   const float* qbase = (const float*)p.q;
   if (b < p.n_pf) {
-    const PrefillItem it = p.pf[b];
-    const ReqInfo ri = p.req[it.req];
+    const PrefillItem it = ldc(p.pf + b);
+    const ReqInfo ri = ldc(p.req + it.req);
     const int rows = it.nq * p.g;
     for (int n = w; n < rows; n += kWavesPerBlock) {
       const int t = n / p.g, h = it.hk * p.g + n % p.g;
@@ -556,8 +695,8 @@ __global__ __launch_bounds__(kBlockThreads) void attn_f32_kernel(AttnParams p) {
   } else {
     const int unit = (b - p.n_pf) * kWavesPerBlock + w;
     if (unit >= p.n_du) return;
-    const DecodeItem it = p.du[unit];
-    const ReqInfo ri = p.req[it.req];
+    const DecodeItem it = ldc(p.du + unit);
+    const ReqInfo ri = ldc(p.req + it.req);
     const int nrows = ri.qo * p.g;
     for (int n = 0; n < nrows; ++n) {
       const int t = n / p.g, h = it.hk * p.g + n % p.g;
@@ -580,8 +719,8 @@ __global__ __launch_bounds__(kBlockThreads) void attn_f32_kernel(AttnParams p) {
 // ------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kBlockThreads) void merge_kernel(AttnParams p) {
-  const MergeGroup mg = p.mg[blockIdx.x];
-  const ReqInfo ri = p.req[mg.req];
+  const MergeGroup mg = ldc(p.mg + blockIdx.x);
+  const ReqInfo ri = ldc(p.req + mg.req);
   const int nrows = ri.qo * p.g;
   constexpr int D4 = D / 4;
   for (int idx = threadIdx.x; idx < nrows * D4; idx += kBlockThreads) {
@@ -615,11 +754,11 @@ __global__ __launch_bounds__(kBlockThreads) void append_kernel(AppendParams p) {
   int lo = 0, hi = p.B - 1;  // last request with qo_indptr[r] <= row
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (p.qo_indptr[mid] <= row) lo = mid; else hi = mid - 1;
+    if (ldc(p.qo_indptr + mid) <= row) lo = mid; else hi = mid - 1;
   }
-  const ReqInfo ri = p.req[lo];
+  const ReqInfo ri = ldc(p.req + lo);
   const int pos = ri.kv - ri.qo + (row - ri.qo_start);
-  const int page = p.page_indices[ri.page_start + pos / p.ps];
+  const int page = ldc(p.page_indices + ri.page_start + pos / p.ps);
   const int slot = pos % p.ps;
   const int64_t head_bytes = (int64_t)p.D * p.elt;
   const int cph = (int)(head_bytes / 16);
