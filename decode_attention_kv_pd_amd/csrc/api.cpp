@@ -55,7 +55,8 @@ pd_status check_desc(const pd_attn_desc* d) {
   if (d->dtype != PD_F32 && d->dtype != PD_BF16)
     return fail(PD_ERR_UNSUPPORTED, "dtype must be PD_F32 or PD_BF16");
   if (d->causal != 0 && d->causal != 1) return fail(PD_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (!std::isfinite(d->sm_scale)) return fail(PD_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (!std::isfinite(d->sm_scale) || !(d->sm_scale > 0.f))
+    return fail(PD_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   return PD_OK;
 }
 
@@ -298,6 +299,7 @@ pdk::AttnParams attn_params(const pd_plan_s& P, void* d_ws) {
   a.H_kv = P.desc.num_kv_heads;
   a.g = P.g;
   a.ps = P.desc.page_size;
+  a.ps_shift = __builtin_ctz((unsigned)P.desc.page_size);
   a.D = P.desc.head_dim;
   a.causal = P.desc.causal;
   a.sm_scale = P.desc.sm_scale;

@@ -99,14 +99,30 @@ __device__ __forceinline__ float sum_x16(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+// True when any of the packed bf16 P values is >= 2^64, inf or NaN (P >= 0,
+// so the bit patterns order like the values).
+template <int N>
+__device__ __forceinline__ bool p_out_of_range(const uint32_t (&pk)[N]) {
+  u16x2 m = __builtin_bit_cast(u16x2, pk[0]);
+#pragma unroll
+  for (int i = 1; i < N; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, pk[i]));
+  return max(m.x, m.y) > 0x5F7F;
+}
+constexpr uint32_t kBf16OnesPair = 0x3F803F80u;  // two bf16 1.0
 __device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
-// Softmax scaling is kept against a reference maximum that is only raised
-// when a row's running maximum exceeds it by more than 2^kRescaleLog2 in the
-// exp2 domain: P values stay <= 2^kRescaleLog2 (exact in fp32, 8-bit
-// mantissa in bf16 either way) and the O rescale is skipped on most tiles.
-// Output = sum(p v) / sum(p) is independent of the reference chosen.
-constexpr float kRescaleLog2 = 8.f;
+// Speculative softmax: P = exp2(s * c - m_ref * c) is computed against the
+// reference maximum m_ref of earlier tiles, without this tile's row maximum.
+// Only when some P of the tile is >= 2^64 (or inf / NaN, which is also how
+// the first tile, m_ref = -inf, is caught) is the row maximum taken, O and l
+// rescaled and P recomputed.  m_ref never exceeds the true running maximum,
+// so P never underflows more than with an exact maximum, and P < 2^64 stays
+// far inside the bf16 / fp32 range.  The normaliser l is the sum of the same
+// bf16-rounded P that multiply V (an extra MFMA against an all-ones operand),
+// so O is an exact convex combination of V rows whatever m_ref is, and a
+// single dominant key is reproduced exactly.
 
 // LDS tile layout (K and V tiles of the prefill role, V stages of the decode
 // role): rows of D bf16 go into 1 KiB load blocks of RPB = 512 / D rows; in a
@@ -159,7 +175,7 @@ struct DecodeCfg {
 __device__ __forceinline__ int2 decode_pages(const AttnParams& p, const ReqInfo& ri, int b) {
   const int32_t* pages = p.page_indices + ri.page_start;
   const int kvm1 = ri.kv - 1;
-  return make_int2(ldc(pages + min(b, kvm1) / p.ps), ldc(pages + min(b + 16, kvm1) / p.ps));
+  return make_int2(ldc(pages + (min(b, kvm1) >> p.ps_shift)), ldc(pages + (min(b + 16, kvm1) >> p.ps_shift)));
 }
 
 // Loads of one 32-key step at key b: K fragments into `kf`, V rows into the
@@ -221,7 +237,7 @@ __device__ __forceinline__ void decode_step(const AttnParams& p, const ReqInfo& 
                                             int lim, int mask_from, DecodeLanes ln, int lane,
                                             const u32x4 (&qf)[D / 32], const u32x4 (&kc)[2][D / 32],
                                             u32x4 (&kn)[2][D / 32], const LDS_AS char* st, LDS_AS char* sn,
-                                            int2& pg_next, float& m_ref, float& l_run,
+                                            int2& pg_next, float& m_ref, f32x4& lacc,
                                             f32x4 (&oacc)[D / 16]) {
   using C = DecodeCfg<D>;
   const float cl = p.c_log2;
@@ -249,30 +265,39 @@ __device__ __forceinline__ void decode_step(const AttnParams& p, const ReqInfo& 
       for (int i = 0; i < 4; ++i)
         if (b + 16 * sb + 4 * ln.q + i >= lim) s[sb][i] = -INFINITY;
   }
-  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-  mx = max_x16(mx);
-  mx = max_x32(mx);
-  if (wave_any(mx * cl > m_ref * cl + kRescaleLog2)) {
-    const float m_new = fmaxf(m_ref, mx);
-    const float alpha = fast_exp2((m_ref - m_new) * cl);  // m_ref = -inf -> 0
-    l_run *= alpha;
+  uint32_t pk[4];
+  {
+    const float mc = m_ref * cl;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) oacc[db] = oacc[db] * alpha;
-    m_ref = m_new;
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        pk[2 * sb + i] = pack_bf16(fast_exp2(__builtin_fmaf(s[sb][2 * i], cl, -mc)),
+                                   fast_exp2(__builtin_fmaf(s[sb][2 * i + 1], cl, -mc)));
   }
-  const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * cl;
-  float psum = 0.f;
+  if (wave_any(p_out_of_range(pk))) {
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = max_x16(mx);
+    mx = max_x32(mx);
+    const float m_new = fmaxf(m_ref, mx);
+    if (m_new != -INFINITY) {  // a column with no visible key yet keeps m_ref = -inf
+      const float alpha = fast_exp2((m_ref - m_new) * cl);  // m_ref = -inf -> 0
+      lacc = lacc * alpha;
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[sb][i] = fast_exp2(__builtin_fmaf(s[sb][i], cl, -mc));
-      psum += s[sb][i];
+      for (int db = 0; db < C::DB; ++db) oacc[db] = oacc[db] * alpha;
+      m_ref = m_new;
     }
-  l_run += psum;
-  const u32x4 pb = {pack_bf16(s[0][0], s[0][1]), pack_bf16(s[0][2], s[0][3]),
-                    pack_bf16(s[1][0], s[1][1]), pack_bf16(s[1][2], s[1][3])};
+    const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * cl;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        pk[2 * sb + i] = pack_bf16(fast_exp2(__builtin_fmaf(s[sb][2 * i], cl, -mc)),
+                                   fast_exp2(__builtin_fmaf(s[sb][2 * i + 1], cl, -mc)));
+  }
+  const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
+  lacc = mfma16(u32x4{kBf16OnesPair, kBf16OnesPair, kBf16OnesPair, kBf16OnesPair}, pb, lacc);
   // V^T[d = 16 db + (lane & 15)][keys 4q + e, 16 + 4q + e]
   const LDS_AS char* vp = st + ln.v_off;
 #pragma unroll
@@ -318,7 +343,8 @@ __device__ void decode_unit(const AttnParams& p, int unit, LDS_AS char* lds) {
   f32x4 oacc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY;
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};  // column sums of the bf16 P (all four entries equal)
 
   u32x4 kf0[2][C::KS], kf1[2][C::KS];
   LDS_AS char* st0 = lds;
@@ -327,17 +353,15 @@ __device__ void decode_unit(const AttnParams& p, int unit, LDS_AS char* lds) {
   decode_issue<D>(p, ri, it.hk, it.k0, decode_pages(p, ri, it.k0), lane, kf0, st0);
   for (int b = it.k0;;) {
     decode_step<D>(p, ri, it.hk, b, it.k1, lim, mask_from, ln, lane, qf, kf0, kf1, st0, st1, pg_next, m_ref,
-                   l_run, oacc);
+                   lacc, oacc);
     b += 32;
     if (b >= it.k1) break;
     decode_step<D>(p, ri, it.hk, b, it.k1, lim, mask_from, ln, lane, qf, kf1, kf0, st1, st0, pg_next, m_ref,
-                   l_run, oacc);
+                   lacc, oacc);
     b += 32;
     if (b >= it.k1) break;
   }
-  // columns: sum the four 16-lane groups
-  float l_tot = sum_x16(l_run);
-  l_tot = sum_x32(l_tot);
+  const float l_tot = lacc[0];
   if (col_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float* po = p.part_o + ((int64_t)it.part * kDecodeCols + n) * D + 4 * q;
@@ -377,7 +401,7 @@ struct PrefillCfg {
 // tile's last key).
 __device__ __forceinline__ int prefill_page(const AttnParams& p, const ReqInfo& ri, int kv_end, int kbase,
                                             int w) {
-  return ldc(p.page_indices + ri.page_start + min(kbase + 16 * w, kv_end - 1) / p.ps);
+  return ldc(p.page_indices + ri.page_start + (min(kbase + 16 * w, kv_end - 1) >> p.ps_shift));
 }
 
 template <int D>
@@ -424,7 +448,7 @@ struct PrefillLanes {
 template <int D, bool MASK>
 __device__ __forceinline__ void prefill_compute(const AttnParams& p, const LDS_AS char* kt,
                                                 const LDS_AS char* vt, int kbase, int lim, PrefillLanes ln,
-                                                const u32x4 (&qf)[D / 16], float& m_ref, float& l_run,
+                                                const u32x4 (&qf)[D / 16], float& m_ref, f32x16& lacc,
                                                 f32x16 (&oacc)[D / 32]) {
   using C = PrefillCfg<D>;
   constexpr int RPB = C::RPB;
@@ -456,39 +480,45 @@ __device__ __forceinline__ void prefill_compute(const AttnParams& p, const LDS_A
       for (int r = 0; r < 16; ++r)
         if (kbase + 32 * kb + 8 * (r >> 2) + 4 * ln.h2 + (r & 3) >= lim) s[kb][r] = -INFINITY;
   }
-  float mx = s[0][0];
+  // P in bf16 pairs, in the key order of the PV operand: pk[kb][8 sp + i]
+  uint32_t pk[2][8];
+  {
+    const float mc = m_ref * cl;
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-  mx = max_x32(mx);
-  if (wave_any(mx * cl > m_ref * cl + kRescaleLog2)) {
+      for (int i = 0; i < 8; ++i)
+        pk[kb][i] = pack_bf16(fast_exp2(__builtin_fmaf(s[kb][2 * i], cl, -mc)),
+                              fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], cl, -mc)));
+  }
+  if (wave_any(p_out_of_range(pk[0]) | p_out_of_range(pk[1]))) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    mx = max_x32(mx);
     const float m_new = fmaxf(m_ref, mx);
     const float alpha = fast_exp2((m_ref - m_new) * cl);  // m_ref = -inf -> 0
-    l_run *= alpha;
+    lacc = lacc * alpha;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) oacc[db] = oacc[db] * alpha;
     m_ref = m_new;
+    const float mc = m_ref * cl;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pk[kb][i] = pack_bf16(fast_exp2(__builtin_fmaf(s[kb][2 * i], cl, -mc)),
+                              fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], cl, -mc)));
   }
-  const float mc = m_ref * cl;
-  float psum = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], cl, -mc));
-      psum += s[kb][r];
-    }
-  l_run += psum;
   // O^T += V^T P^T over the four 16-key k-steps
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int sp = 0; sp < 2; ++sp) {
-      const u32x4 pb = {pack_bf16(s[kb][8 * sp + 0], s[kb][8 * sp + 1]),
-                        pack_bf16(s[kb][8 * sp + 2], s[kb][8 * sp + 3]),
-                        pack_bf16(s[kb][8 * sp + 4], s[kb][8 * sp + 5]),
-                        pack_bf16(s[kb][8 * sp + 6], s[kb][8 * sp + 7])};
+      const u32x4 pb = {pk[kb][4 * sp + 0], pk[kb][4 * sp + 1], pk[kb][4 * sp + 2], pk[kb][4 * sp + 3]};
+      lacc = mfma32(u32x4{kBf16OnesPair, kBf16OnesPair, kBf16OnesPair, kBf16OnesPair}, pb, lacc);
       const LDS_AS char* vp = vt + ln.v_off + ((32 * kb + 16 * sp) / RPB) * Lds<D>::BLOCK;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
@@ -540,7 +570,8 @@ __device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
   f32x16 oacc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
-  float m_ref = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY;
+  f32x16 lacc = {};  // row sums of the bf16 P (all sixteen entries equal)
 
   LDS_AS char* kbuf = lds;
   LDS_AS char* vbuf = lds + 2 * C::TILE_BYTES;
@@ -562,7 +593,7 @@ __device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
                        kbuf + (buf ^ 1) * C::TILE_BYTES, vbuf + (buf ^ 1) * C::TILE_BYTES);
     }
     prefill_compute<D, false>(p, kbuf + buf * C::TILE_BYTES, vbuf + buf * C::TILE_BYTES, kt * 64, lim, ln,
-                              qf, m_ref, l_run, oacc);
+                              qf, m_ref, lacc, oacc);
   }
   for (; kt < ntiles; ++kt) {
     const int buf = kt & 1;
@@ -575,9 +606,9 @@ __device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
                        kbuf + (buf ^ 1) * C::TILE_BYTES, vbuf + (buf ^ 1) * C::TILE_BYTES);
     }
     prefill_compute<D, true>(p, kbuf + buf * C::TILE_BYTES, vbuf + buf * C::TILE_BYTES, kt * 64, lim, ln,
-                             qf, m_ref, l_run, oacc);
+                             qf, m_ref, lacc, oacc);
   }
-  const float l_tot = sum_x32(l_run);
+  const float l_tot = lacc[0];
   if (row_ok) {
     const float inv = 1.f / l_tot;
     float* op = p.out + qrow * D;

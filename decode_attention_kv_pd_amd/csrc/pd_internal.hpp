@@ -56,6 +56,7 @@ struct AttnParams {
   float* part_lse;  // [n_du][kDecodeCols]
   int32_t n_pf, n_du, n_mg, B;
   int32_t H_q, H_kv, g, ps;
+  int32_t ps_shift;  // log2(ps)
   int32_t D, causal;
   float sm_scale;
   float c_log2;        // sm_scale * log2(e)

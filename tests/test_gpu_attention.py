@@ -1,7 +1,9 @@
 """GPU: attention parity with the float64 oracle, element by element.
 
 Bars: max |O - O_oracle| <= 1e-4 for fp32 inputs and <= 2e-2 for bf16 inputs
-(fp32 accumulation); LSE within 1e-4 (fp32) / 2e-3 (bf16).  Cases span the
+(fp32 accumulation); LSE within 1e-4 (fp32) / 5e-3 (bf16: the kernels
+normalise by the sum of the bf16-rounded softmax weights, whose log differs
+from the exact log-sum-exp by at most ln(1 + 2^-8) < 3.9e-3).  Cases span the
 five seeded workloads (the long one at reduced length here; full length in
 test_gpu_long), several tiles and ragged tails, every supported head_dim,
 page size and GQA group, causal and non-causal, qo = 0 requests, the
@@ -27,7 +29,7 @@ def batch(wid, lengths=None, **kw):
 
 
 def lse_tol(b):
-    return 1e-4 if b.dtype == "f32" else 2e-3
+    return 1e-4 if b.dtype == "f32" else 5e-3
 
 
 def check(b, name, chunk=0):

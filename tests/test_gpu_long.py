@@ -81,7 +81,7 @@ def test_long_context_full_size():
             err = float(np.abs(got - O).max())
             worst = max(worst, err)
             assert err <= 2e-2, f"request {r} kv head {hk}: {err}"
-            assert float(np.abs(got_l - L).max()) <= 2e-3
+            assert float(np.abs(got_l - L).max()) <= 5e-3
     print(f"long: worst sampled max_abs_err={worst:.3e}", flush=True)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
 
