@@ -305,6 +305,22 @@ def main():
                 legs[name] = {"ms": round(t, 4), "TFLOPs": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
             p.close()
             del wsp, qs, os_, ls
+        # the same mixed batch with the prefill tiles launched before the decode blocks
+        p = pd.pd_plan(desc, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages,
+                       block_order=1)
+        pd.pd_plan_upload(p, ws)
+        pd.pd_attention_run(p, ws, q, pool, out, lse)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(args.phase_reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pd.pd_attention_run(p, ws, q, pool, out, lse)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        legs["mixed_prefill_first_order_ms"] = round(float(np.median(ts)), 4)
+        p.close()
         legs["interference_ratio"] = round(t_attn / legs["decode_only"]["ms"], 3)
         legs["mixed_vs_sum"] = round(t_attn / (legs["decode_only"]["ms"] + legs["prefill_only"]["ms"]), 3)
         result["phases"] = legs

@@ -5,8 +5,8 @@
 // prefill and decode", section "Prefill vs Decode performance": prefill and
 // decode requests batched together, attention parallel over requests and
 // kv_len) into
-//   * prefill tiles: up to 128 query rows (tokens x the g query heads of one
-//     KV head) over the tile's causal key range, one 256-thread block each,
+//   * prefill tiles: up to 256 query rows (tokens x the g query heads of one
+//     KV head) over the tile's causal key range, one 512-thread block each,
 //     ordered so that the tiles of one (request, KV head) share an XCD and
 //     longest tiles start first;
 //   * decode units: the <= 16 query rows of one (request, KV head) over a
@@ -47,7 +47,7 @@ pd_status check_desc(const pd_attn_desc* d) {
   if (d->num_qo_heads % d->num_kv_heads != 0)
     return fail(PD_ERR_INVALID_ARG, "num_qo_heads must be a multiple of num_kv_heads");
   if (d->num_qo_heads / d->num_kv_heads > pdk::kPrefillRows)
-    return fail(PD_ERR_UNSUPPORTED, "query heads per KV head must be <= 128");
+    return fail(PD_ERR_UNSUPPORTED, "query heads per KV head must be <= 256");
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(PD_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (d->page_size != 16 && d->page_size != 32 && d->page_size != 64 && d->page_size != 128)
@@ -77,7 +77,8 @@ struct pd_plan_s {
   std::vector<pdk::PrefillItem> pf;
   std::vector<pdk::DecodeItem> du;
   std::vector<pdk::MergeGroup> mg;
-  size_t off_qo = 0, off_req = 0, off_pages = 0, off_pf = 0, off_du = 0, off_mg = 0;
+  std::vector<int32_t> block_map;  // attention launch order
+  size_t off_qo = 0, off_req = 0, off_pages = 0, off_pf = 0, off_du = 0, off_mg = 0, off_bmap = 0;
   size_t meta_bytes = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   int64_t prefill_flops = 0, decode_bytes = 0;
   std::vector<char> blob;  // host image of the workspace tables
@@ -150,6 +151,7 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
 
   // ---- prefill tiles: requests whose qo * g rows exceed one decode unit
   const int T = std::max(1, pdk::kPrefillRows / g);  // tokens per tile
+  std::vector<double> pf_cost;                        // flops of each tile, launch order
   struct Tile {
     pdk::PrefillItem it;
     int64_t cost;
@@ -203,6 +205,7 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
           if (xq[y].size() - head[y] > best) best = xq[y].size() - head[y], bx = y;
         x = bx;
       }
+      pf_cost.push_back((double)xq[x][head[x]].cost * 4.0 * d.head_dim);  // flops
       P.pf.push_back(xq[x][head[x]++].it);
     }
   }
@@ -246,6 +249,42 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   });
   P.du = std::move(units);
 
+  // ---- launch order.  Block i is dispatched to XCD i % 8, so blocks are
+  // emitted in rounds of 8: a prefill round keeps the XCD affinity of the
+  // tiles built above, a decode round takes the next 8 decode blocks.  With
+  // block_order 0 the rounds are interleaved so that the prefill tiles
+  // (MFMA-bound) and the decode blocks (HBM-bound) progress at the same
+  // fraction of their totals, priced at MI355X peaks (2.5 PFLOP/s, 8 TB/s),
+  // and the CUs run both kinds at once.
+  const int n_db = ((int)P.du.size() + pdk::kWavesPerBlock - 1) / pdk::kWavesPerBlock;
+  std::vector<double> db_cost(n_db, 0.0);
+  for (size_t u = 0; u < P.du.size(); ++u)
+    db_cost[u / pdk::kWavesPerBlock] += 2.0 * (P.du[u].k1 - P.du[u].k0) * d.head_dim * elt;
+  const int order = opts ? opts->block_order : 0;
+  P.block_map.reserve(P.pf.size() + n_db);
+  if (order == 1 || P.pf.empty() || n_db == 0) {
+    for (size_t i = 0; i < P.pf.size(); ++i) P.block_map.push_back((int32_t)i);
+    for (int i = 0; i < n_db; ++i) P.block_map.push_back(-i - 1);
+  } else {
+    double tot_p = 0, tot_d = 0, done_p = 0, done_d = 0;
+    for (double c : pf_cost) tot_p += c / 2.5e15;
+    for (double c : db_cost) tot_d += c / 8e12;
+    size_t ip = 0;
+    int id = 0;
+    while (ip < P.pf.size() || id < n_db) {
+      const bool take_p = id >= n_db || (ip < P.pf.size() && done_p / tot_p <= done_d / tot_d);
+      for (int k = 0; k < kNumXcd; ++k) {
+        if (take_p && ip < P.pf.size()) {
+          done_p += pf_cost[ip] / 2.5e15;
+          P.block_map.push_back((int32_t)ip++);
+        } else if (!take_p && id < n_db) {
+          done_d += db_cost[id] / 8e12;
+          P.block_map.push_back(-(id++) - 1);
+        }
+      }
+    }
+  }
+
   // ---- workspace layout
   size_t off = 0;
   P.off_qo = off;
@@ -260,6 +299,8 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   off = align_up(off + sizeof(pdk::DecodeItem) * P.du.size());
   P.off_mg = off;
   off = align_up(off + sizeof(pdk::MergeGroup) * P.mg.size());
+  P.off_bmap = off;
+  off = align_up(off + sizeof(int32_t) * P.block_map.size());
   P.meta_bytes = off;
   P.off_part_o = off;
   off = align_up(off + sizeof(float) * (size_t)P.n_parts * pdk::kDecodeCols * d.head_dim);
@@ -277,6 +318,7 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   put(P.off_pf, P.pf.data(), sizeof(pdk::PrefillItem) * P.pf.size());
   put(P.off_du, P.du.data(), sizeof(pdk::DecodeItem) * P.du.size());
   put(P.off_mg, P.mg.data(), sizeof(pdk::MergeGroup) * P.mg.size());
+  put(P.off_bmap, P.block_map.data(), sizeof(int32_t) * P.block_map.size());
   return PD_OK;
 }
 
@@ -289,6 +331,8 @@ pdk::AttnParams attn_params(const pd_plan_s& P, void* d_ws) {
   a.pf = (const pdk::PrefillItem*)(ws + P.off_pf);
   a.du = (const pdk::DecodeItem*)(ws + P.off_du);
   a.mg = (const pdk::MergeGroup*)(ws + P.off_mg);
+  a.block_map = (const int32_t*)(ws + P.off_bmap);
+  a.n_blocks = (int32_t)P.block_map.size();
   a.part_o = (float*)(ws + P.off_part_o);
   a.part_lse = (float*)(ws + P.off_part_lse);
   a.n_pf = (int32_t)P.pf.size();
@@ -373,6 +417,8 @@ pd_status pd_plan(const pd_attn_desc* desc, int32_t batch, const int32_t* qo_len
     if (num_pool_pages < 0) return fail(PD_ERR_INVALID_ARG, "num_pool_pages must be >= 0");
     if (opts && (opts->decode_chunk_keys < 0 || opts->num_cus < 0))
       return fail(PD_ERR_INVALID_ARG, "negative planner option");
+    if (opts && opts->block_order != 0 && opts->block_order != 1)
+      return fail(PD_ERR_INVALID_ARG, "block_order must be 0 or 1");
     const int ps = desc->page_size;
     if (page_indptr[0] != 0) return fail(PD_ERR_INVALID_ARG, "page_indptr[0] must be 0");
     int64_t rows = 0;
@@ -452,6 +498,7 @@ int32_t pd_plan_work_items(pd_plan_t plan, int32_t kind, int32_t* out, int32_t m
     case 0: src = (const int32_t*)plan->pf.data(); count = plan->pf.size(); width = 8; break;
     case 1: src = (const int32_t*)plan->du.data(); count = plan->du.size(); width = 8; break;
     case 2: src = (const int32_t*)plan->mg.data(); count = plan->mg.size(); width = 4; break;
+    case 3: src = plan->block_map.data(); count = plan->block_map.size(); width = 1; break;
     default: return fail(PD_ERR_INVALID_ARG, "unknown work item kind");
   }
   if (max_items > 0 && out) {

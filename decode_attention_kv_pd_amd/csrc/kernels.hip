@@ -374,68 +374,76 @@ __device__ void decode_unit(const AttnParams& p, int unit, LDS_AS char* lds) {
 }
 
 // ------------------------------------------------------------------------
-// Prefill role: one 256-thread block computes one PrefillItem (<= 128 query
+// Prefill role: one 512-thread block computes one PrefillItem (<= 256 query
 // rows: tokens x the g heads of one KV head) over 64-key tiles.
 //   Wave w owns query rows 32 w .. 32 w + 31 (the N index of both products).
 //   S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16; Q^T stays in
-//   registers; K and V tiles are staged in LDS (double buffered, direct
-//   global->LDS loads, one 16-row page group per wave); K is read back 16
-//   bytes per lane, V with the transposed read; P^T is the S accumulator
-//   re-packed to bf16 in place.  Tiles that cross the causal diagonal (or the
-//   end of the cache) run a separate masked copy of the loop body.
+//   registers; K and V tiles are staged in LDS by direct global->LDS loads
+//   (three tiles in flight, each wave loading one 8-row group), read back 16
+//   bytes per lane (K) and transposed (V); P^T is the S accumulator re-packed
+//   to bf16 in place.  Eight wavefronts share every K/V tile: the tile stream
+//   from L2 is what bounds this role, so rows per tile are what pays.  The
+//   loop is software-pipelined: S of tile t + 1 runs on the MFMA pipe while
+//   the VALU computes the softmax of tile t, then PV of tile t.  Tiles that
+//   cross the causal diagonal (or the end of the cache) run a masked copy.
 // ------------------------------------------------------------------------
 template <int D>
 struct PrefillCfg {
   static constexpr int KS = D / 16;     // 16-wide k-steps of S
   static constexpr int DB = D / 32;     // 32-row d-blocks of O^T
   static constexpr int RPB = Lds<D>::RPB;
-  static constexpr int LOADS = 16 / RPB;  // 1 KiB loads per wave per matrix per tile
+  static constexpr int ROWS_PER_WAVE = 64 / kAttnWaves;  // K/V rows each wave loads per tile
+  static constexpr int LOADS = ROWS_PER_WAVE / RPB;      // 1 KiB loads per wave per matrix per tile
+  static constexpr int NBUF = 3;                         // K and V tiles in flight
   static constexpr int TILE_BYTES = Lds<D>::bytes(64);
-  static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K, V x 2 buffers
+  static constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
 };
 
-// Loads of the 64-key tile at kbase (wave w: rows 16 w .. 16 w + 15, one page
-// group).  `full`: every row < kv_end; otherwise rows past kv_end - 1 are read
-// from row kv_end - 1 (finite, masked later).
-// Page id of wave w's 16-row group of the tile at kbase (clamped to the
-// tile's last key).
+// Page id of wave w's row group of the tile at kbase (clamped to the tile's
+// last key).
+template <int D>
 __device__ __forceinline__ int prefill_page(const AttnParams& p, const ReqInfo& ri, int kv_end, int kbase,
                                             int w) {
-  return ldc(p.page_indices + ri.page_start + (min(kbase + 16 * w, kv_end - 1) >> p.ps_shift));
+  constexpr int RW = PrefillCfg<D>::ROWS_PER_WAVE;
+  return ldc(p.page_indices + ri.page_start + (min(kbase + RW * w, kv_end - 1) >> p.ps_shift));
 }
 
+// Loads of one matrix (K or V: `half`) of the 64-key tile at kbase (wave w:
+// its 8-row group, inside one page since pages hold >= 16 aligned rows).
+// `full`: every row < kv_end; otherwise rows past kv_end - 1 are read from
+// row kv_end - 1 (finite, masked later).
 template <int D>
-__device__ __forceinline__ void prefill_issue(const AttnParams& p, int hk, int kv_end, int kbase, int w,
-                                              int page, int lane, bool full, LDS_AS char* kt,
-                                              LDS_AS char* vt) {
+__device__ __forceinline__ void prefill_issue(const AttnParams& p, int hk, int half, int kv_end, int kbase,
+                                              int w, int page, int lane, bool full, LDS_AS char* dst) {
   using C = PrefillCfg<D>;
   const char* pool = (const char*)p.pool;
   const int psm = p.ps - 1;
   const int r = lane % C::RPB, c = lane / C::RPB;
-  const int j0 = kbase + 16 * w;
-  LDS_AS char* kd = kt + (16 / C::RPB) * w * Lds<D>::BLOCK;
-  LDS_AS char* vd = vt + (16 / C::RPB) * w * Lds<D>::BLOCK;
+  const int j0 = kbase + C::ROWS_PER_WAVE * w;
+  LDS_AS char* d = dst + (C::ROWS_PER_WAVE / C::RPB) * w * Lds<D>::BLOCK;
+  const char* base = pool + page_head_off(p, page, half, hk);
   if (full) {
-    const int slot0 = j0 & psm;
-    const char* kb = pool + page_head_off(p, page, 0, hk) + slot0 * 2 * D;
-    const char* vb = pool + page_head_off(p, page, 1, hk) + slot0 * 2 * D;
-    const int lo = r * 2 * D + 16 * c;
+    const char* b = base + (j0 & psm) * 2 * D + r * 2 * D + 16 * c;
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      load_lds16(kb + i * C::RPB * 2 * D + lo, kd + i * Lds<D>::BLOCK);
-      load_lds16(vb + i * C::RPB * 2 * D + lo, vd + i * Lds<D>::BLOCK);
-    }
+    for (int i = 0; i < C::LOADS; ++i) load_lds16(b + i * C::RPB * 2 * D, d + i * Lds<D>::BLOCK);
   } else {
     const int last = kv_end - 1;
-    const char* kb = pool + page_head_off(p, page, 0, hk);
-    const char* vb = pool + page_head_off(p, page, 1, hk);
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int row = min(j0 + i * C::RPB + r, last) & psm;
-      load_lds16(kb + row * 2 * D + 16 * c, kd + i * Lds<D>::BLOCK);
-      load_lds16(vb + row * 2 * D + 16 * c, vd + i * Lds<D>::BLOCK);
+      load_lds16(base + row * 2 * D + 16 * c, d + i * Lds<D>::BLOCK);
     }
   }
+}
+template <int D>
+__device__ __forceinline__ void prefill_issue_k(const AttnParams& p, int hk, int kv_end, int kbase, int w,
+                                                int page, int lane, bool full, LDS_AS char* dst) {
+  prefill_issue<D>(p, hk, 0, kv_end, kbase, w, page, lane, full, dst);
+}
+template <int D>
+__device__ __forceinline__ void prefill_issue_v(const AttnParams& p, int hk, int kv_end, int kbase, int w,
+                                                int page, int lane, bool full, LDS_AS char* dst) {
+  prefill_issue<D>(p, hk, 1, kv_end, kbase, w, page, lane, full, dst);
 }
 
 struct PrefillLanes {
@@ -444,18 +452,14 @@ struct PrefillLanes {
   int v_off;  // lane part of the transposed V read address
 };
 
-// S, softmax and PV of one 64-key tile already in LDS.
-template <int D, bool MASK>
-__device__ __forceinline__ void prefill_compute(const AttnParams& p, const LDS_AS char* kt,
-                                                const LDS_AS char* vt, int kbase, int lim, PrefillLanes ln,
-                                                const u32x4 (&qf)[D / 16], float& m_ref, f32x16& lacc,
-                                                f32x16 (&oacc)[D / 32]) {
+// S^T = K Q^T for one 64-key tile in LDS: S^T[key 32 kb + 8 jj + 4 h2 + i]
+// [query] lands in s[kb][4 jj + i].  The two accumulator chains are
+// interleaved and K is read one k-step ahead.
+template <int D>
+__device__ __forceinline__ void prefill_scores(const LDS_AS char* kt, PrefillLanes ln,
+                                               const u32x4 (&qf)[D / 16], f32x16 (&s)[2]) {
   using C = PrefillCfg<D>;
   constexpr int RPB = C::RPB;
-  const float cl = p.c_log2;
-  // S^T[key 32 kb + 8 jj + 4 h2 + i][query] in s[kb][4 jj + i]; the two
-  // accumulator chains are interleaved and K is read one k-step ahead
-  f32x16 s[2];
   const LDS_AS char* kp = kt + ln.k_off;
   constexpr int KB1 = (32 / RPB) * Lds<D>::BLOCK;
   u32x4 a0 = lds_read16(kp), a1 = lds_read16(kp + KB1);
@@ -473,6 +477,16 @@ __device__ __forceinline__ void prefill_compute(const AttnParams& p, const LDS_A
     s[0] = mfma32(a0, qf[ks], s[0]);
     s[1] = mfma32(a1, qf[ks], s[1]);
   }
+}
+
+// Speculative softmax of one tile's scores (see kMaxTileSum above): returns
+// P in bf16 pairs, in the key order of the PV operand (pk[kb][4 sp + i]).
+template <int D, bool MASK>
+__device__ __forceinline__ void prefill_softmax(const AttnParams& p, f32x16 (&s)[2], int kbase, int lim,
+                                                PrefillLanes ln, float& m_ref, f32x16& lacc,
+                                                f32x16 (&oacc)[D / 32], uint32_t (&pk)[2][8]) {
+  using C = PrefillCfg<D>;
+  const float cl = p.c_log2;
   if (MASK) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -480,8 +494,6 @@ __device__ __forceinline__ void prefill_compute(const AttnParams& p, const LDS_A
       for (int r = 0; r < 16; ++r)
         if (kbase + 32 * kb + 8 * (r >> 2) + 4 * ln.h2 + (r & 3) >= lim) s[kb][r] = -INFINITY;
   }
-  // P in bf16 pairs, in the key order of the PV operand: pk[kb][8 sp + i]
-  uint32_t pk[2][8];
   {
     const float mc = m_ref * cl;
 #pragma unroll
@@ -512,7 +524,15 @@ __device__ __forceinline__ void prefill_compute(const AttnParams& p, const LDS_A
         pk[kb][i] = pack_bf16(fast_exp2(__builtin_fmaf(s[kb][2 * i], cl, -mc)),
                               fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], cl, -mc)));
   }
-  // O^T += V^T P^T over the four 16-key k-steps
+}
+
+// O^T += V^T P^T over the four 16-key k-steps of one tile (and the row sums of
+// the bf16 P into lacc).
+template <int D>
+__device__ __forceinline__ void prefill_pv(const LDS_AS char* vt, PrefillLanes ln, const uint32_t (&pk)[2][8],
+                                           f32x16& lacc, f32x16 (&oacc)[D / 32]) {
+  using C = PrefillCfg<D>;
+  constexpr int RPB = C::RPB;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -528,6 +548,60 @@ __device__ __forceinline__ void prefill_compute(const AttnParams& p, const LDS_A
         oacc[db] = mfma32(a, pb, oacc[db]);
       }
     }
+}
+
+// s_waitcnt vmcnt(n) for n in {0, L, 2L} (the count must be an immediate).
+template <int L>
+__device__ __forceinline__ void wait_vm(int n) {
+  if (n >= 2 * L) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L) : "memory");
+  else if (n >= L) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+struct PrefillLoop {
+  int ntiles, nfull;
+  int pg_k, pg_v;  // page ids of the next K and V loads (scalar loads one iteration ahead)
+  int slot;        // t % NBUF
+};
+
+// One pipelined iteration t.  Issue order of the loads is K(t+3), V(t+2) per
+// iteration (K(0) V(0) K(1) V(1) K(2) before the loop), so at the top of
+// iteration t K(t+1) and V(t) are complete once at most the loads of
+// iteration t - 1 (K(t+2), V(t+1)) are outstanding.  Then S(t+1) on the MFMA
+// pipe, the softmax of S(t) on the VALU, and PV(t).
+template <int D, bool MASK, bool NEXT>
+__device__ __forceinline__ void prefill_iter(const AttnParams& p, const ReqInfo& ri, const PrefillItem& it,
+                                             int t, int w, int lane, bool active, int lim, PrefillLanes ln,
+                                             const u32x4 (&qf)[D / 16], LDS_AS char* kbuf, LDS_AS char* vbuf,
+                                             PrefillLoop& L, f32x16 (&s_cur)[2], float& m_ref, f32x16& lacc,
+                                             f32x16 (&oacc)[D / 32]) {
+  using C = PrefillCfg<D>;
+  const int nt = L.ntiles;
+  wait_vm<C::LOADS>(C::LOADS * ((t + 1 < nt) + (t + 2 < nt)));
+  __syncthreads();
+  const int s0 = L.slot, s1 = s0 == C::NBUF - 1 ? 0 : s0 + 1, s2 = s1 == C::NBUF - 1 ? 0 : s1 + 1;
+  if (t + 3 < nt) {
+    prefill_issue_k<D>(p, it.hk, it.kv_end, (t + 3) * 64, w, L.pg_k, lane, t + 3 < L.nfull,
+                       kbuf + s0 * C::TILE_BYTES);
+    L.pg_k = prefill_page<D>(p, ri, it.kv_end, (t + 4) * 64, w);
+  }
+  if (t + 2 < nt) {
+    prefill_issue_v<D>(p, it.hk, it.kv_end, (t + 2) * 64, w, L.pg_v, lane, t + 2 < L.nfull,
+                       vbuf + s2 * C::TILE_BYTES);
+    L.pg_v = prefill_page<D>(p, ri, it.kv_end, (t + 3) * 64, w);
+  }
+  if (active) {
+    f32x16 s_next[2];
+    if (NEXT) prefill_scores<D>(kbuf + s1 * C::TILE_BYTES, ln, qf, s_next);  // NEXT: t + 1 < ntiles
+    uint32_t pk[2][8];
+    prefill_softmax<D, MASK>(p, s_cur, t * 64, lim, ln, m_ref, lacc, oacc, pk);
+    prefill_pv<D>(vbuf + s0 * C::TILE_BYTES, ln, pk, lacc, oacc);
+    if (NEXT) {
+      s_cur[0] = s_next[0];
+      s_cur[1] = s_next[1];
+    }
+  }
+  L.slot = s1;
 }
 
 template <int D>
@@ -574,40 +648,45 @@ __device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
   f32x16 lacc = {};  // row sums of the bf16 P (all sixteen entries equal)
 
   LDS_AS char* kbuf = lds;
-  LDS_AS char* vbuf = lds + 2 * C::TILE_BYTES;
+  LDS_AS char* vbuf = lds + C::NBUF * C::TILE_BYTES;
   const int ntiles = (it.kv_end + 63) >> 6;
   const int nfull = it.kv_end >> 6;                                  // tiles with every row < kv_end
   const int nplain = min(ntiles, mask_from / 64);  // tiles whose keys all lie below every row's limit
-  int pg_next = prefill_page(p, ri, it.kv_end, 64, w);
-  prefill_issue<D>(p, it.hk, it.kv_end, 0, w, prefill_page(p, ri, it.kv_end, 0, w), lane, 0 < nfull, kbuf,
-                   vbuf);
+  // prologue: K(0) V(0) K(1) V(1) K(2); S(0)
+  PrefillLoop L;
+  L.ntiles = ntiles;
+  L.nfull = nfull;
+  L.slot = 0;
+  for (int j = 0; j < 3 && j < ntiles; ++j) {
+    prefill_issue_k<D>(p, it.hk, it.kv_end, j * 64, w, prefill_page<D>(p, ri, it.kv_end, j * 64, w), lane,
+                       j < nfull, kbuf + j * C::TILE_BYTES);
+    if (j < 2)
+      prefill_issue_v<D>(p, it.hk, it.kv_end, j * 64, w, prefill_page<D>(p, ri, it.kv_end, j * 64, w), lane,
+                         j < nfull, vbuf + j * C::TILE_BYTES);
+  }
+  L.pg_k = prefill_page<D>(p, ri, it.kv_end, 3 * 64, w);  // K(t + 3) at t = 0
+  L.pg_v = prefill_page<D>(p, ri, it.kv_end, 2 * 64, w);  // V(t + 2)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const bool active = 32 * w < rows;  // waves whose rows are all padding skip the math
+  f32x16 s_cur[2];
+  if (active) prefill_scores<D>(kbuf, ln, qf, s_cur);
+  // iterations with a next tile (unmasked, then masked), then the last one
+  const int last = ntiles - 1;
+  const int n1 = min(nplain, last);
   int kt = 0;
-  for (; kt < nplain; ++kt) {
-    const int buf = kt & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < ntiles) {
-      const int pg = pg_next;
-      if (kt + 2 < ntiles) pg_next = prefill_page(p, ri, it.kv_end, (kt + 2) * 64, w);
-      prefill_issue<D>(p, it.hk, it.kv_end, (kt + 1) * 64, w, pg, lane, kt + 1 < nfull,
-                       kbuf + (buf ^ 1) * C::TILE_BYTES, vbuf + (buf ^ 1) * C::TILE_BYTES);
-    }
-    prefill_compute<D, false>(p, kbuf + buf * C::TILE_BYTES, vbuf + buf * C::TILE_BYTES, kt * 64, lim, ln,
-                              qf, m_ref, lacc, oacc);
-  }
-  for (; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < ntiles) {
-      const int pg = pg_next;
-      if (kt + 2 < ntiles) pg_next = prefill_page(p, ri, it.kv_end, (kt + 2) * 64, w);
-      prefill_issue<D>(p, it.hk, it.kv_end, (kt + 1) * 64, w, pg, lane, kt + 1 < nfull,
-                       kbuf + (buf ^ 1) * C::TILE_BYTES, vbuf + (buf ^ 1) * C::TILE_BYTES);
-    }
-    prefill_compute<D, true>(p, kbuf + buf * C::TILE_BYTES, vbuf + buf * C::TILE_BYTES, kt * 64, lim, ln,
-                             qf, m_ref, lacc, oacc);
-  }
+  for (; kt < n1; ++kt)
+    prefill_iter<D, false, true>(p, ri, it, kt, w, lane, active, lim, ln, qf, kbuf, vbuf, L, s_cur, m_ref,
+                                 lacc, oacc);
+  for (; kt < last; ++kt)
+    prefill_iter<D, true, true>(p, ri, it, kt, w, lane, active, lim, ln, qf, kbuf, vbuf, L, s_cur, m_ref,
+                                lacc, oacc);
+  if (last < nplain)
+    prefill_iter<D, false, false>(p, ri, it, last, w, lane, active, lim, ln, qf, kbuf, vbuf, L, s_cur, m_ref,
+                                  lacc, oacc);
+  else
+    prefill_iter<D, true, false>(p, ri, it, last, w, lane, active, lim, ln, qf, kbuf, vbuf, L, s_cur, m_ref,
+                                 lacc, oacc);
   const float l_tot = lacc[0];
   if (row_ok) {
     const float inv = 1.f / l_tot;
@@ -623,19 +702,23 @@ __device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
   }
 }
 
-// One launch for both roles: blocks [0, n_pf) are prefill tiles, the rest
-// hold four decode units each (one per wavefront).
+// One launch for both roles: the block map gives each block a prefill tile
+// (v >= 0) or a decode block of eight units, one per wavefront (v < 0).
 template <int D>
-__global__ __launch_bounds__(kBlockThreads, 2) void attn_bf16_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char lds_raw[PrefillCfg<D>::LDS_BYTES];
-  static_assert(kWavesPerBlock * DecodeCfg<D>::WAVE_LDS <= PrefillCfg<D>::LDS_BYTES, "lds");
+constexpr int attn_lds_bytes() {
+  return PrefillCfg<D>::LDS_BYTES > kAttnWaves * DecodeCfg<D>::WAVE_LDS ? PrefillCfg<D>::LDS_BYTES
+                                                                         : kAttnWaves * DecodeCfg<D>::WAVE_LDS;
+}
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) char lds_raw[attn_lds_bytes<D>()];
   LDS_AS char* lds = (LDS_AS char*)lds_raw;
-  const int b = blockIdx.x;
-  if (b < p.n_pf) {
-    prefill_tile<D>(p, b, lds);
+  const int v = ldc(p.block_map + blockIdx.x);
+  if (v >= 0) {
+    prefill_tile<D>(p, v, lds);
   } else {
     const int w = uniform_i(threadIdx.x >> 6);
-    const int unit = (b - p.n_pf) * kWavesPerBlock + w;
+    const int unit = (-v - 1) * kAttnWaves + w;
     if (unit < p.n_du) decode_unit<D>(p, unit, lds + w * DecodeCfg<D>::WAVE_LDS);
   }
 }
@@ -703,14 +786,14 @@ __device__ void f32_row(const AttnParams& p, const ReqInfo& ri, int hk, const fl
 }
 
 template <int D>
-__global__ __launch_bounds__(kBlockThreads) void attn_f32_kernel(AttnParams p) {
+__global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(AttnParams p) {
   constexpr int NO = D / 64;
   const int lane = threadIdx.x & 63;
   const int w = uniform_i(threadIdx.x >> 6);
-  const int b = blockIdx.x;
+  const int v = ldc(p.block_map + blockIdx.x);
   const float* qbase = (const float*)p.q;
-  if (b < p.n_pf) {
-    const PrefillItem it = ldc(p.pf + b);
+  if (v >= 0) {
+    const PrefillItem it = ldc(p.pf + v);
     const ReqInfo ri = ldc(p.req + it.req);
     const int rows = it.nq * p.g;
     for (int n = w; n < rows; n += kWavesPerBlock) {
@@ -724,7 +807,7 @@ __global__ __launch_bounds__(kBlockThreads) void attn_f32_kernel(AttnParams p) {
       if (lane == 0 && p.lse) p.lse[row] = lse;
     }
   } else {
-    const int unit = (b - p.n_pf) * kWavesPerBlock + w;
+    const int unit = (-v - 1) * kWavesPerBlock + w;
     if (unit >= p.n_du) return;
     const DecodeItem it = ldc(p.du + unit);
     const ReqInfo ri = ldc(p.req + it.req);
@@ -840,18 +923,18 @@ __global__ __launch_bounds__(kBlockThreads) void pack_kernel(PackParams p) {
 }  // namespace
 
 hipError_t launch_attention(const AttnParams& p, int dtype, hipStream_t s) {
-  const int blocks = p.n_pf + (p.n_du + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int blocks = p.n_blocks;
   if (blocks == 0) return hipSuccess;
   if (dtype == 1) {
     if (p.D == 128)
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(blocks), dim3(kBlockThreads), 0, s, p);
+      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(blocks), dim3(kAttnThreads), 0, s, p);
     else
-      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(blocks), dim3(kBlockThreads), 0, s, p);
+      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(blocks), dim3(kAttnThreads), 0, s, p);
   } else {
     if (p.D == 128)
-      hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(blocks), dim3(kBlockThreads), 0, s, p);
+      hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(blocks), dim3(kAttnThreads), 0, s, p);
     else
-      hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(blocks), dim3(kBlockThreads), 0, s, p);
+      hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(blocks), dim3(kAttnThreads), 0, s, p);
   }
   return hipGetLastError();
 }

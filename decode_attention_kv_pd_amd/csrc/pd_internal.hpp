@@ -15,7 +15,7 @@ struct ReqInfo {
   int32_t page_start;  // first entry of the request in page_indices
 };
 
-// A causal query tile of a prefill request, computed by one 256-thread block
+// A causal query tile of a prefill request, computed by one 512-thread block
 // on bf16 MFMA: tokens [q0, q0 + nq) of request `req` times the g query heads
 // of KV head `hk` (row n of the tile = token q0 + n / g, head hk * g + n % g),
 // over keys [0, kv_end).  Written straight to out / lse.
@@ -36,10 +36,12 @@ struct MergeGroup {
   int32_t req, hk, part0, nparts;
 };
 
-constexpr int kBlockThreads = 256;  // both roles of the attention kernel
-constexpr int kPrefillRows = 128;   // query rows per prefill tile
+constexpr int kBlockThreads = 256;  // append, pack, merge and the fp32 kernel
+constexpr int kAttnWaves = 8;       // wavefronts per block of the bf16 attention kernel
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kPrefillRows = 32 * kAttnWaves;  // query rows per prefill tile (32 per wavefront)
 constexpr int kDecodeCols = 16;     // query rows per decode unit (MFMA N)
-constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerBlock = kAttnWaves;  // decode units per block (both attention kernels)
 
 struct AttnParams {
   const void* q;
@@ -52,9 +54,11 @@ struct AttnParams {
   const PrefillItem* pf;
   const DecodeItem* du;
   const MergeGroup* mg;
+  const int32_t* block_map;  // launch block -> prefill tile (>= 0) or decode block (-b - 1)
   float* part_o;    // [n_du][kDecodeCols][D]
   float* part_lse;  // [n_du][kDecodeCols]
   int32_t n_pf, n_du, n_mg, B;
+  int32_t n_blocks;  // blocks of the attention launch
   int32_t H_q, H_kv, g, ps;
   int32_t ps_shift;  // log2(ps)
   int32_t D, causal;

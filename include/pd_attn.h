@@ -39,13 +39,13 @@
  * Ownership: the caller allocates and owns every device buffer (pool, q,
  * k_new, v_new, out, lse, workspace, pack buffer, scratch); the library never
  * allocates or frees device memory.  The library owns the opaque plan (host
- * memory and a pinned staging buffer), released by pd_plan_free.  A plan is
- * immutable once built; pd_plan_upload may be called again on another
+ * memory), released by pd_plan_free, and a process-wide pool of pinned host
+ * staging blocks for uploads, reused across plans and never released.  A plan
+ * is immutable once built; pd_plan_upload may be called again on another
  * workspace.
  *
  * Streams: every `void* stream` is a hipStream_t (NULL = the default stream);
- * all device work is enqueued on it and no call except pd_plan_free waits for
- * the device.
+ * all device work is enqueued on it and no call waits for the device.
  *
  * Errors: every argument is checked before anything is enqueued, so a failing
  * call has no side effect on device memory.  Calls return PD_OK or a negative
@@ -77,7 +77,7 @@ typedef enum pd_dtype { PD_F32 = 0, PD_BF16 = 1 } pd_dtype;
 
 /* Shape of one attention layer.
  *   num_qo_heads  query heads H_q (> 0, multiple of num_kv_heads)
- *   num_kv_heads  KV heads H_kv (> 0); g = H_q / H_kv <= 16 is required for
+ *   num_kv_heads  KV heads H_kv (> 0); g = H_q / H_kv <= 256; g <= 16 for
  *                 single-token (decode) rows, larger groups are supported
  *                 for prefill rows only
  *   head_dim      64 or 128
@@ -98,11 +98,17 @@ typedef struct pd_attn_desc {
 /* Optional planner controls (NULL = defaults).
  *   decode_chunk_keys  keys per split-KV chunk of a decode row group; 0 lets
  *                      the planner choose; otherwise rounded up to 32
- *   num_cus            compute units to balance over; 0 = 256 (MI355X)    */
+ *   num_cus            compute units to balance over; 0 = 256 (MI355X)
+ *   block_order        order of the blocks of the attention launch:
+ *                      0 = interleave prefill and decode blocks by cost so
+ *                          that MFMA-bound and HBM-bound blocks share the CUs
+ *                          (default); 1 = all prefill tiles, then all decode
+ *                          blocks                                            */
 typedef struct pd_plan_options {
   int32_t decode_chunk_keys;
   int32_t num_cus;
-  int32_t reserved[6];
+  int32_t block_order;
+  int32_t reserved[5];
 } pd_plan_options;
 
 /* Plan statistics (pd_plan_get_stats). */
@@ -113,7 +119,8 @@ typedef struct pd_plan_stats {
   int32_t decode_units;        /* split-KV units (one wavefront each) */
   int32_t decode_row_groups;   /* (request, kv head) groups merged */
   int32_t decode_chunk_keys;   /* chunk length used */
-  int64_t prefill_flops;       /* 4 * head_dim * visible (query, key) pairs * H_q / g ... summed exactly */
+  int64_t prefill_flops;       /* 4 * head_dim * H_q * visible (query, key)
+                                  pairs of the prefill rows (algorithmic) */
   int64_t decode_kv_bytes;     /* K + V bytes the decode rows read */
   int64_t workspace_bytes;
 } pd_plan_stats;
@@ -153,8 +160,9 @@ pd_status pd_plan(const pd_attn_desc* desc, int32_t batch,
  * partial results).  0 for a NULL plan. */
 size_t pd_plan_workspace_bytes(pd_plan_t plan);
 
-/* Copy the plan's tables into the caller's device workspace (asynchronous
- * host-to-device copy from the plan's pinned staging buffer on `stream`).
+/* Copy the plan's tables into the caller's device workspace: the tables are
+ * copied into a free pinned staging block before the call returns, and the
+ * host-to-device copy is enqueued on `stream`.
  * Must precede pd_kv_append / pd_attention_run with the same d_ws.
  * Errors: PD_ERR_INVALID_ARG (null plan / d_ws), PD_ERR_WORKSPACE
  * (ws_bytes < pd_plan_workspace_bytes), PD_ERR_HIP. */
@@ -167,19 +175,21 @@ pd_status pd_plan_get_stats(pd_plan_t plan, pd_plan_stats* out);
 /* Diagnostics: copy the plan's work list (host only).
  *   kind 0: prefill tiles, 8 int32 each:
  *           {request, kv_head, first token, tokens, key end (exclusive), 0,0,0}
- *           in launch order (block i of the launch runs on XCD i % 8)
  *   kind 1: decode units, 8 int32 each:
  *           {request, kv_head, key begin, key end (exclusive), partial slot,
- *            0,0,0} in launch order (four units per block)
+ *            0,0,0}, four consecutive units per decode block
  *   kind 2: merge groups, 4 int32 each:
  *           {request, kv_head, first partial slot, partial count}
+ *   kind 3: the attention launch's blocks in launch order, 1 int32 each:
+ *           v >= 0 is prefill tile v, v < 0 is decode block -v - 1
  * Writes at most max_items items to out (which may be NULL when max_items is
  * 0) and returns the total number of items of that kind, or a negative
  * pd_status (PD_ERR_INVALID_ARG for a NULL plan or an unknown kind). */
 int32_t pd_plan_work_items(pd_plan_t plan, int32_t kind, int32_t* out,
                            int32_t max_items);
 
-/* Release a plan; waits for its last upload to finish.  NULL is a no-op. */
+/* Release a plan (host memory only; uploads already enqueued are not
+ * affected).  NULL is a no-op. */
 void pd_plan_free(pd_plan_t plan);
 
 /* Append the step's new K and V rows into the pool: for each request r and

@@ -69,7 +69,7 @@ def test_plan_accepts_valid_batch():
     (dict(page_size=8), "PD_ERR_UNSUPPORTED"),
     (dict(dtype=7), "PD_ERR_UNSUPPORTED"),
     (dict(num_qo_heads=0), "PD_ERR_INVALID_ARG"),
-    (dict(num_qo_heads=256, num_kv_heads=1), "PD_ERR_UNSUPPORTED"),
+    (dict(num_qo_heads=512, num_kv_heads=1), "PD_ERR_UNSUPPORTED"),
 ])
 def test_plan_rejects_bad_desc(kw, status):
     qo, kv, ip, ids, pool = plan_args()
@@ -156,7 +156,7 @@ def check_cover(b, plan):
     for (r, hk, q0, nq, kv_end, *_rest) in pf:
         qo, kv = int(b.qo_lens[r]), int(b.kv_lens[r])
         assert qo * g > 16
-        assert nq * g <= 128 and 0 <= q0 and q0 + nq <= qo
+        assert nq * g <= 256 and 0 <= q0 and q0 + nq <= qo
         assert kv_end == (kv - qo + q0 + nq if b.causal else kv)
         for t in range(q0, q0 + nq):
             for h in range(hk * g, hk * g + g):
@@ -220,12 +220,27 @@ def test_planner_work_figures_match_closed_forms():
     assert s.decode_kv_bytes == 256 * 32768 * 2 * 8 * 128 * 2
 
 
-def test_prefill_tiles_of_a_group_share_an_xcd():
+@pytest.mark.parametrize("order", [0, 1])
+def test_block_map_covers_work_and_keeps_xcd_affinity(order):
+    """Every prefill tile and decode block appears once in the launch order;
+    block i runs on XCD i % 8, and all tiles of one (request, KV head) land
+    on the same XCD (the long workload's 8 KV heads on 8 different XCDs)."""
     b = make_batch("long", materialize=False)
     d = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype)
-    pf = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages).work_items(0)
+    plan = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages,
+                      block_order=order)
+    pf, du, bmap = plan.work_items(0), plan.work_items(1), plan.work_items(3)[:, 0]
+    n_db = (len(du) + 7) // 8   # eight decode units (one per wavefront) per block
+    assert sorted(bmap[bmap >= 0].tolist()) == list(range(len(pf)))
+    assert sorted((-bmap[bmap < 0] - 1).tolist()) == list(range(n_db))
     xcd_of_head = {}
-    for i, row in enumerate(pf):
-        xcd_of_head.setdefault(int(row[1]), set()).add(i % 8)
+    for pos, v in enumerate(bmap):
+        if v >= 0:
+            xcd_of_head.setdefault(int(pf[v][1]), set()).add(pos % 8)
     assert all(len(v) == 1 for v in xcd_of_head.values())
     assert len({next(iter(v)) for v in xcd_of_head.values()}) == 8
+    if order == 0:   # interleaved: decode blocks appear before the last prefill tile
+        first_d = int(np.argmax(bmap < 0))
+        assert first_d < len(pf)
+    else:
+        assert (bmap[:len(pf)] >= 0).all()
