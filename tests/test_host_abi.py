@@ -239,8 +239,8 @@ def test_block_map_covers_work_and_keeps_xcd_affinity(order):
             xcd_of_head.setdefault(int(pf[v][1]), set()).add(pos % 8)
     assert all(len(v) == 1 for v in xcd_of_head.values())
     assert len({next(iter(v)) for v in xcd_of_head.values()}) == 8
-    if order == 0:   # interleaved: decode blocks appear before the last prefill tile
+    if order == 1:   # interleaved: decode blocks appear before the last prefill tile
         first_d = int(np.argmax(bmap < 0))
         assert first_d < len(pf)
-    else:
+    else:            # prefill tiles first
         assert (bmap[:len(pf)] >= 0).all()
