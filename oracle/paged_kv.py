@@ -29,6 +29,19 @@ The operations:
               (post, section "KV Messenger")
   pack_bytes  size of a packed buffer
 
+Sharded transfers (post, section "Sharded KV Cache Transfers"): when the
+prefiller and the decoder split the KV heads over different numbers of
+tensor-parallel ranks, a page is split or rebuilt by moving head ranges of it.
+  kv_pack_heads / kv_unpack_heads   the same copies restricted to KV heads
+              [h0, h1) of each page (K slice then V slice of each page)
+  shard_heads, shard_transfers      which head range of a page goes from
+              which source rank to which destination rank; a destination page
+              expects one write per transfer that targets its rank
+  kv_pack_layers / kv_unpack_layers the copies for several layers' pools at
+              once, layer after layer -- transfers of a layer may start as
+              soon as that layer's KV has been appended (post, section "KV
+              Messenger")
+
 All copies are exact: the arrays are moved as stored (fp32 values or bf16 bit
 patterns), never converted.
 """
@@ -102,3 +115,79 @@ def kv_unpack(pool, page_ids, buf):
     for i, p in enumerate(page_ids):
         pool[int(p)] = buf[i]
     return pool
+
+
+def pack_heads_bytes(n_pages: int, h0: int, h1: int, page_size: int, head_dim: int,
+                     elt_bytes: int) -> int:
+    """Bytes of the head-[h0, h1) slices of ``n_pages`` pages (K and V)."""
+    return pack_bytes(n_pages, h1 - h0, page_size, head_dim, elt_bytes)
+
+
+def kv_pack_heads(pool, page_ids, h0, h1):
+    """Buffer [n, 2, h1 - h0, ps, D]: KV heads [h0, h1) of the listed pages."""
+    out = np.empty((len(page_ids), 2, h1 - h0) + pool.shape[3:], pool.dtype)
+    for i, p in enumerate(page_ids):
+        for half in range(2):
+            for j, h in enumerate(range(h0, h1)):
+                out[i, half, j] = pool[int(p), half, h]
+    return out
+
+
+def kv_unpack_heads(pool, page_ids, h0, h1, buf):
+    """Write buffer page i into KV heads [h0, h1) of pool page ``page_ids[i]``
+    (in place); the other heads of the page are left as they are."""
+    for i, p in enumerate(page_ids):
+        for half in range(2):
+            for j, h in enumerate(range(h0, h1)):
+                pool[int(p), half, h] = buf[i, half, j]
+    return pool
+
+
+def kv_pack_layers(pools, page_ids, h0, h1):
+    """Buffer [L, n, 2, h1 - h0, ps, D]: layer after layer, the head slices of
+    the listed pages of each layer's pool."""
+    return np.stack([kv_pack_heads(pool, page_ids, h0, h1) for pool in pools])
+
+
+def kv_unpack_layers(pools, page_ids, h0, h1, buf):
+    """Inverse of kv_pack_layers, in place in every layer's pool."""
+    for layer, pool in enumerate(pools):
+        kv_unpack_heads(pool, page_ids, h0, h1, buf[layer])
+    return pools
+
+
+def shard_heads(H_kv: int, shards: int, rank: int) -> list:
+    """KV heads held by ``rank`` when H_kv heads are split evenly and in order
+    over ``shards`` tensor-parallel ranks (contiguous blocks of heads)."""
+    if shards < 1 or H_kv % shards:
+        raise ValueError("the shards must divide the KV heads")
+    per = H_kv // shards
+    return list(range(rank * per, (rank + 1) * per))
+
+
+def shard_transfers(H_kv: int, src_shards: int, dst_shards: int) -> list:
+    """Every (source rank, destination rank) pair whose heads overlap, with the
+    overlap as local head ranges on both sides:
+    (src_rank, dst_rank, src_h0, src_h1, dst_h0, dst_h1).  Found by
+    intersecting the head sets; each overlap is a contiguous range."""
+    out = []
+    for s in range(src_shards):
+        S = shard_heads(H_kv, src_shards, s)
+        for d in range(dst_shards):
+            Dh = shard_heads(H_kv, dst_shards, d)
+            common = sorted(set(S) & set(Dh))
+            if not common:
+                continue
+            assert common == list(range(common[0], common[-1] + 1))
+            lo, hi = common[0], common[-1] + 1
+            out.append((s, d, lo - S[0], hi - S[0], lo - Dh[0], hi - Dh[0]))
+    return out
+
+
+def reshard(src_pools, page_ids_src, dst_pools, page_ids_dst, H_kv):
+    """Apply shard_transfers: for every transfer, pack the head slice on the
+    source rank and unpack it into the destination rank's pages (in place)."""
+    for s, d, a0, a1, b0, b1 in shard_transfers(H_kv, len(src_pools), len(dst_pools)):
+        buf = kv_pack_heads(src_pools[s], page_ids_src, a0, a1)
+        kv_unpack_heads(dst_pools[d], page_ids_dst, b0, b1, buf)
+    return dst_pools
