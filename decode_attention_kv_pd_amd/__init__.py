@@ -12,6 +12,14 @@ The names mirror the C entry points of include/pd_attn.h:
   pd_kv_pack_bytes(desc, n_pages)                   -> int
   pd_kv_pack(desc, kv_pool, num_pool_pages, page_ids, buf, scratch, stream=None)
   pd_kv_unpack(desc, kv_pool, num_pool_pages, page_ids, buf, scratch, stream=None)
+  pd_kv_pack_heads_bytes(desc, n_pages, h0, h1)     -> int
+  pd_kv_pack_heads(desc, kv_pool, num_pool_pages, page_ids, h0, h1, buf, scratch, stream=None)
+  pd_kv_unpack_heads(desc, kv_pool, num_pool_pages, page_ids, h0, h1, buf, scratch, stream=None)
+  pd_kv_shard_transfers(num_kv_heads, src_shards, dst_shards) -> list of 6-tuples
+  pd_xfer_plan(desc, kv_pools, num_pool_pages, page_ids, h0=0, h1=None) -> XferPlan (host only)
+  pd_xfer_upload(xfer, ws, stream=None)
+  pd_kv_pack_layers(xfer, ws, buf, progress=None, stream=None)
+  pd_kv_unpack_layers(xfer, ws, buf, progress=None, stream=None)
 
 Device arguments are torch tensors (contiguous, on the GPU); host arrays are
 anything numpy can turn into int32.  Errors raise PdError carrying the
@@ -66,7 +74,16 @@ class pd_plan_stats(ctypes.Structure):
 
 EXPORTS = ("pd_plan", "pd_plan_workspace_bytes", "pd_plan_upload", "pd_plan_get_stats",
            "pd_plan_free", "pd_plan_work_items", "pd_kv_append", "pd_attention_run", "pd_kv_pack_bytes",
-           "pd_kv_pack", "pd_kv_unpack", "pd_status_string", "pd_last_error", "pd_version")
+           "pd_kv_pack", "pd_kv_unpack", "pd_kv_pack_heads_bytes", "pd_kv_pack_heads", "pd_kv_unpack_heads",
+           "pd_kv_shard_transfers", "pd_xfer_plan", "pd_xfer_buffer_bytes", "pd_xfer_workspace_bytes",
+           "pd_xfer_upload", "pd_kv_pack_layers", "pd_kv_unpack_layers", "pd_xfer_free",
+           "pd_status_string", "pd_last_error", "pd_version")
+
+
+class pd_head_transfer(ctypes.Structure):
+    _fields_ = [("src_rank", ctypes.c_int32), ("dst_rank", ctypes.c_int32),
+                ("src_h0", ctypes.c_int32), ("src_h1", ctypes.c_int32),
+                ("dst_h0", ctypes.c_int32), ("dst_h1", ctypes.c_int32)]
 
 
 def _load():
@@ -90,6 +107,20 @@ def _load():
         "pd_kv_pack_bytes": (SZ, [ctypes.POINTER(pd_attn_desc), I32]),
         "pd_kv_pack": (I32, [ctypes.POINTER(pd_attn_desc), VP, I32, pI32, I32, VP, SZ, VP, SZ, VP]),
         "pd_kv_unpack": (I32, [ctypes.POINTER(pd_attn_desc), VP, I32, pI32, I32, VP, SZ, VP, SZ, VP]),
+        "pd_kv_pack_heads_bytes": (SZ, [ctypes.POINTER(pd_attn_desc), I32, I32, I32]),
+        "pd_kv_pack_heads": (I32, [ctypes.POINTER(pd_attn_desc), VP, I32, pI32, I32, I32, I32, VP, SZ, VP, SZ,
+                                   VP]),
+        "pd_kv_unpack_heads": (I32, [ctypes.POINTER(pd_attn_desc), VP, I32, pI32, I32, I32, I32, VP, SZ, VP, SZ,
+                                     VP]),
+        "pd_kv_shard_transfers": (I32, [I32, I32, I32, ctypes.POINTER(pd_head_transfer), I32, pI32]),
+        "pd_xfer_plan": (I32, [ctypes.POINTER(pd_attn_desc), I32, ctypes.POINTER(VP), I32, pI32, I32, I32, I32,
+                               ctypes.POINTER(P)]),
+        "pd_xfer_buffer_bytes": (SZ, [P]),
+        "pd_xfer_workspace_bytes": (SZ, [P]),
+        "pd_xfer_upload": (I32, [P, VP, SZ, VP]),
+        "pd_kv_pack_layers": (I32, [P, VP, VP, SZ, VP, VP]),
+        "pd_kv_unpack_layers": (I32, [P, VP, VP, SZ, VP, VP]),
+        "pd_xfer_free": (None, [P]),
         "pd_status_string": (ctypes.c_char_p, [I32]),
         "pd_last_error": (ctypes.c_char_p, []),
         "pd_version": (ctypes.c_char_p, []),
@@ -260,3 +291,107 @@ def pd_kv_unpack(desc, kv_pool, num_pool_pages, page_ids, buf, scratch, stream=N
                              len(ids), _dev(buf, "buf"), buf.numel() * buf.element_size(),
                              _dev(scratch, "scratch"), scratch.numel() * scratch.element_size(),
                              _stream(stream)))
+
+
+def pd_kv_pack_heads_bytes(desc, n_pages: int, h0: int, h1: int) -> int:
+    return int(_lib.pd_kv_pack_heads_bytes(ctypes.byref(desc), int(n_pages), int(h0), int(h1)))
+
+
+def pd_kv_pack_heads(desc, kv_pool, num_pool_pages, page_ids, h0, h1, buf, scratch, stream=None):
+    ids, pids = _i32(page_ids)
+    _check(_lib.pd_kv_pack_heads(ctypes.byref(desc), _dev(kv_pool, "kv_pool"), int(num_pool_pages), pids,
+                                 len(ids), int(h0), int(h1), _dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                 _dev(scratch, "scratch"), scratch.numel() * scratch.element_size(),
+                                 _stream(stream)))
+
+
+def pd_kv_unpack_heads(desc, kv_pool, num_pool_pages, page_ids, h0, h1, buf, scratch, stream=None):
+    ids, pids = _i32(page_ids)
+    _check(_lib.pd_kv_unpack_heads(ctypes.byref(desc), _dev(kv_pool, "kv_pool"), int(num_pool_pages), pids,
+                                   len(ids), int(h0), int(h1), _dev(buf, "buf"),
+                                   buf.numel() * buf.element_size(), _dev(scratch, "scratch"),
+                                   scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def pd_kv_shard_transfers(num_kv_heads: int, src_shards: int, dst_shards: int) -> list:
+    """[(src_rank, dst_rank, src_h0, src_h1, dst_h0, dst_h1), ...]"""
+    n = ctypes.c_int32(0)
+    _check(_lib.pd_kv_shard_transfers(int(num_kv_heads), int(src_shards), int(dst_shards), None, 0,
+                                      ctypes.byref(n)))
+    arr = (pd_head_transfer * max(n.value, 1))()
+    _check(_lib.pd_kv_shard_transfers(int(num_kv_heads), int(src_shards), int(dst_shards), arr, n.value,
+                                      ctypes.byref(n)))
+    return [tuple(getattr(arr[i], f) for f, _ in pd_head_transfer._fields_) for i in range(n.value)]
+
+
+class XferPlan:
+    """Owns a pd_xfer_t; freed on close() or garbage collection."""
+
+    def __init__(self, handle, desc, num_layers):
+        self._h = handle
+        self.desc = desc
+        self.num_layers = num_layers
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("transfer plan is closed")
+        return self._h
+
+    @property
+    def buffer_bytes(self) -> int:
+        return int(_lib.pd_xfer_buffer_bytes(self.handle))
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(_lib.pd_xfer_workspace_bytes(self.handle))
+
+    def close(self):
+        if self._h is not None:
+            _lib.pd_xfer_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def pd_xfer_plan(desc, kv_pools, num_pool_pages, page_ids, h0=0, h1=None) -> XferPlan:
+    """kv_pools: list of per-layer pool tensors (GPU) or raw device addresses."""
+    ptrs = (ctypes.c_void_p * max(len(kv_pools), 1))()
+    for i, t in enumerate(kv_pools):
+        ptrs[i] = t if isinstance(t, int) else _dev(t, f"kv_pools[{i}]").value
+    ids, pids = _i32(page_ids)
+    h1 = desc.num_kv_heads if h1 is None else h1
+    h = ctypes.c_void_p()
+    _check(_lib.pd_xfer_plan(ctypes.byref(desc), len(kv_pools), ptrs, int(num_pool_pages),
+                             pids if len(ids) else None, len(ids), int(h0), int(h1), ctypes.byref(h)))
+    return XferPlan(h, desc, len(kv_pools))
+
+
+def pd_xfer_upload(xfer: XferPlan, ws, stream=None):
+    _check(_lib.pd_xfer_upload(xfer.handle, _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def _progress_ptr(progress):
+    """Address of a progress array: a pinned host tensor or a GPU tensor."""
+    if progress is None:
+        return None
+    if not progress.is_contiguous() or progress.element_size() != 4:
+        raise ValueError("progress must be a contiguous 32-bit tensor")
+    if not progress.is_cuda and not progress.is_pinned():
+        raise ValueError("progress on the host must be pinned (pin_memory=True)")
+    return ctypes.c_void_p(progress.data_ptr())
+
+
+def pd_kv_pack_layers(xfer: XferPlan, ws, buf, progress=None, stream=None):
+    _check(_lib.pd_kv_pack_layers(xfer.handle, _dev(ws, "ws"), _dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                  _progress_ptr(progress), _stream(stream)))
+
+
+def pd_kv_unpack_layers(xfer: XferPlan, ws, buf, progress=None, stream=None):
+    _check(_lib.pd_kv_unpack_layers(xfer.handle, _dev(ws, "ws"), _dev(buf, "buf"),
+                                    buf.numel() * buf.element_size(), _progress_ptr(progress),
+                                    _stream(stream)))

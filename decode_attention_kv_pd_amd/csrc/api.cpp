@@ -39,6 +39,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dispatched round robin
+constexpr int32_t kMaxXferLayers = 4096;  // layers of one multi-layer transfer (grid z)
 
 pd_status check_desc(const pd_attn_desc* d) {
   if (!d) return fail(PD_ERR_INVALID_ARG, "desc is NULL");
@@ -82,6 +83,15 @@ struct pd_plan_s {
   size_t meta_bytes = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   int64_t prefill_flops = 0, decode_bytes = 0;
   std::vector<char> blob;  // host image of the workspace tables
+};
+
+// A multi-layer transfer: the listed pages' heads [h0, h1) of L layer pools.
+// Workspace image: L pool pointers, the n page ids, L block counters (zero).
+struct pd_xfer_s {
+  pd_attn_desc desc{};
+  int32_t L = 0, n = 0, h0 = 0, h1 = 0;
+  size_t off_layers = 0, off_ids = 0, off_done = 0, ws_bytes = 0;
+  std::vector<uint8_t> blob;
 };
 
 namespace {
@@ -358,19 +368,21 @@ pd_status hip_fail(hipError_t e, const char* what) {
   return fail(PD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-pd_status check_page_list(const pd_attn_desc* desc, int32_t num_pool_pages, const int32_t* ids,
-                          int32_t n, size_t buf_bytes, size_t scratch_bytes, const void* pool,
-                          const void* buf, const void* scratch) {
-  pd_status s = check_desc(desc);
-  if (s != PD_OK) return s;
-  if (n < 0) return fail(PD_ERR_INVALID_ARG, "n must be >= 0");
-  if (n == 0) return PD_OK;
-  if (!ids || !pool || !buf || !scratch) return fail(PD_ERR_INVALID_ARG, "NULL pointer argument");
+// Bytes of the head-[h0, h1) slice of one half (K or V) of a page.
+int64_t head_seg_bytes(const pd_attn_desc* d, int32_t h0, int32_t h1) {
+  return (int64_t)(h1 - h0) * d->page_size * d->head_dim * elt_bytes(d);
+}
+
+pd_status check_heads(const pd_attn_desc* d, int32_t h0, int32_t h1) {
+  if (h0 < 0 || h1 > d->num_kv_heads || h0 >= h1)
+    return fail(PD_ERR_INVALID_ARG, "head range [" + std::to_string(h0) + ", " + std::to_string(h1) +
+                                        ") is not a non-empty range of the pool's " +
+                                        std::to_string(d->num_kv_heads) + " KV heads");
+  return PD_OK;
+}
+
+pd_status check_ids(int32_t num_pool_pages, const int32_t* ids, int32_t n) {
   if (num_pool_pages < 1) return fail(PD_ERR_INVALID_ARG, "num_pool_pages must be >= 1");
-  if (buf_bytes < (size_t)n * (size_t)page_bytes_of(desc))
-    return fail(PD_ERR_WORKSPACE, "buffer smaller than n pages");
-  if (scratch_bytes < sizeof(int32_t) * (size_t)n)
-    return fail(PD_ERR_WORKSPACE, "scratch smaller than 4 * n bytes");
   std::vector<uint8_t> seen((size_t)num_pool_pages, 0);
   for (int32_t i = 0; i < n; ++i) {
     if (ids[i] < 0 || ids[i] >= num_pool_pages)
@@ -381,27 +393,94 @@ pd_status check_page_list(const pd_attn_desc* desc, int32_t num_pool_pages, cons
   return PD_OK;
 }
 
-pd_status pack_common(const pd_attn_desc* desc, const void* src, void* dst, int32_t num_pool_pages,
-                      const int32_t* ids, int32_t n, size_t buf_bytes, void* scratch,
+// Single-layer pack / unpack of heads [h0, h1) of the listed pages.
+pd_status xfer_common(const pd_attn_desc* desc, const void* pool, const void* buf, int32_t num_pool_pages,
+                      const int32_t* ids, int32_t n, int32_t h0, int32_t h1, size_t buf_bytes, void* scratch,
                       size_t scratch_bytes, void* stream, bool to_buffer) {
-  pd_status s = check_page_list(desc, num_pool_pages, ids, n, buf_bytes, scratch_bytes,
-                                to_buffer ? src : dst, to_buffer ? dst : src, scratch);
-  if (s != PD_OK || n == 0) return s;
+  pd_status s = check_desc(desc);
+  if (s != PD_OK) return s;
+  if ((s = check_heads(desc, h0, h1)) != PD_OK) return s;
+  if (n < 0) return fail(PD_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return PD_OK;
+  if (!ids || !pool || !buf || !scratch) return fail(PD_ERR_INVALID_ARG, "NULL pointer argument");
+  if (buf_bytes < (size_t)n * 2 * (size_t)head_seg_bytes(desc, h0, h1))
+    return fail(PD_ERR_WORKSPACE, "buffer smaller than the n page slices");
+  if (scratch_bytes < sizeof(int32_t) * (size_t)n)
+    return fail(PD_ERR_WORKSPACE, "scratch smaller than 4 * n bytes");
+  if ((s = check_ids(num_pool_pages, ids, n)) != PD_OK) return s;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = hipMemcpyAsync(scratch, ids, sizeof(int32_t) * (size_t)n, hipMemcpyHostToDevice, st);
-  if (e != hipSuccess) return hip_fail(e, "page id upload");
-  pdk::PackParams p{};
-  p.dst = dst;
-  p.src = src;
+  if ((s = staged_upload(scratch, ids, sizeof(int32_t) * (size_t)n, st)) != PD_OK) return s;
+  pdk::XferParams p{};
+  p.buf = (char*)buf;
+  p.pool0 = (void*)pool;
   p.page_ids = (const int32_t*)scratch;
-  p.n = n;
-  p.to_buffer = to_buffer ? 1 : 0;
   p.page_bytes = page_bytes_of(desc);
-  e = pdk::launch_pack(p, st);
+  p.half_bytes = p.page_bytes / 2;
+  p.seg_off = head_seg_bytes(desc, 0, h0);
+  p.seg_bytes = head_seg_bytes(desc, h0, h1);
+  p.n = n;
+  p.L = 1;
+  p.to_buffer = to_buffer ? 1 : 0;
+  hipError_t e = pdk::launch_xfer(p, st);
   if (e != hipSuccess) return hip_fail(e, to_buffer ? "pack launch" : "unpack launch");
   return PD_OK;
 }
 
+// Device-accessible address of a progress array: pinned host memory
+// (hipHostMalloc) is translated, device memory is used as is; anything else
+// is rejected.
+pd_status progress_device_ptr(uint32_t* progress, uint32_t** out) {
+  *out = nullptr;
+  if (!progress) return PD_OK;
+  hipPointerAttribute_t a{};
+  hipError_t e = hipPointerGetAttributes(&a, progress);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PD_ERR_INVALID_ARG, "progress must be pinned host memory (hipHostMalloc) or device memory");
+  }
+  if (a.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    e = hipHostGetDevicePointer(&d, progress, 0);
+    if (e != hipSuccess || !d) {
+      (void)hipGetLastError();
+      return fail(PD_ERR_INVALID_ARG, "progress host memory is not mapped into the device");
+    }
+    *out = (uint32_t*)d;
+    return PD_OK;
+  }
+  if (a.type == hipMemoryTypeDevice) {
+    *out = progress;
+    return PD_OK;
+  }
+  return fail(PD_ERR_INVALID_ARG, "progress must be pinned host memory (hipHostMalloc) or device memory");
+}
+
+pd_status xfer_layers(pd_xfer_t x, void* d_ws, const void* d_buf, size_t buf_bytes, uint32_t* progress,
+                      void* stream, bool to_buffer) {
+  if (!x || !d_ws || !d_buf) return fail(PD_ERR_INVALID_ARG, "NULL pointer argument");
+  if (buf_bytes < pd_xfer_buffer_bytes(x)) return fail(PD_ERR_WORKSPACE, "buffer smaller than pd_xfer_buffer_bytes");
+  uint32_t* prog = nullptr;
+  pd_status s = progress_device_ptr(progress, &prog);
+  if (s != PD_OK) return s;
+  if (x->n == 0) return PD_OK;
+  char* ws = (char*)d_ws;
+  pdk::XferParams p{};
+  p.buf = (char*)d_buf;
+  p.layers = (void* const*)(ws + x->off_layers);
+  p.page_ids = (const int32_t*)(ws + x->off_ids);
+  p.done = (uint32_t*)(ws + x->off_done);
+  p.progress = prog;
+  p.page_bytes = page_bytes_of(&x->desc);
+  p.half_bytes = p.page_bytes / 2;
+  p.seg_off = head_seg_bytes(&x->desc, 0, x->h0);
+  p.seg_bytes = head_seg_bytes(&x->desc, x->h0, x->h1);
+  p.n = x->n;
+  p.L = x->L;
+  p.to_buffer = to_buffer ? 1 : 0;
+  hipError_t e = pdk::launch_xfer(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, to_buffer ? "layer pack launch" : "layer unpack launch");
+  return PD_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -577,7 +656,8 @@ pd_status pd_kv_pack(const pd_attn_desc* desc, const void* kv_pool, int32_t num_
                      const int32_t* page_ids, int32_t n, void* d_buf, size_t buf_bytes, void* d_scratch,
                      size_t scratch_bytes, void* stream) {
   try {
-    return pack_common(desc, kv_pool, d_buf, num_pool_pages, page_ids, n, buf_bytes, d_scratch,
+    const int32_t H = desc ? desc->num_kv_heads : 0;
+    return xfer_common(desc, kv_pool, d_buf, num_pool_pages, page_ids, n, 0, H, buf_bytes, d_scratch,
                        scratch_bytes, stream, true);
   } catch (...) {
     return fail(PD_ERR_NO_MEMORY, "host allocation failed");
@@ -588,12 +668,138 @@ pd_status pd_kv_unpack(const pd_attn_desc* desc, void* kv_pool, int32_t num_pool
                        const int32_t* page_ids, int32_t n, const void* d_buf, size_t buf_bytes,
                        void* d_scratch, size_t scratch_bytes, void* stream) {
   try {
-    return pack_common(desc, d_buf, kv_pool, num_pool_pages, page_ids, n, buf_bytes, d_scratch,
+    const int32_t H = desc ? desc->num_kv_heads : 0;
+    return xfer_common(desc, kv_pool, d_buf, num_pool_pages, page_ids, n, 0, H, buf_bytes, d_scratch,
                        scratch_bytes, stream, false);
   } catch (...) {
     return fail(PD_ERR_NO_MEMORY, "host allocation failed");
   }
 }
+
+size_t pd_kv_pack_heads_bytes(const pd_attn_desc* desc, int32_t n_pages, int32_t h0, int32_t h1) {
+  if (n_pages < 0 || !desc) return 0;
+  if (desc->num_kv_heads < 1 || desc->page_size < 1 || desc->head_dim < 1) return 0;
+  if (desc->dtype != PD_F32 && desc->dtype != PD_BF16) return 0;
+  if (h0 < 0 || h1 > desc->num_kv_heads || h0 >= h1) return 0;
+  return (size_t)n_pages * 2 * (size_t)head_seg_bytes(desc, h0, h1);
+}
+
+pd_status pd_kv_pack_heads(const pd_attn_desc* desc, const void* kv_pool, int32_t num_pool_pages,
+                           const int32_t* page_ids, int32_t n, int32_t h0, int32_t h1, void* d_buf,
+                           size_t buf_bytes, void* d_scratch, size_t scratch_bytes, void* stream) {
+  try {
+    return xfer_common(desc, kv_pool, d_buf, num_pool_pages, page_ids, n, h0, h1, buf_bytes, d_scratch,
+                       scratch_bytes, stream, true);
+  } catch (...) {
+    return fail(PD_ERR_NO_MEMORY, "host allocation failed");
+  }
+}
+
+pd_status pd_kv_unpack_heads(const pd_attn_desc* desc, void* kv_pool, int32_t num_pool_pages,
+                             const int32_t* page_ids, int32_t n, int32_t h0, int32_t h1, const void* d_buf,
+                             size_t buf_bytes, void* d_scratch, size_t scratch_bytes, void* stream) {
+  try {
+    return xfer_common(desc, kv_pool, d_buf, num_pool_pages, page_ids, n, h0, h1, buf_bytes, d_scratch,
+                       scratch_bytes, stream, false);
+  } catch (...) {
+    return fail(PD_ERR_NO_MEMORY, "host allocation failed");
+  }
+}
+
+pd_status pd_kv_shard_transfers(int32_t num_kv_heads, int32_t src_shards, int32_t dst_shards,
+                                pd_head_transfer* out, int32_t max_out, int32_t* n_out) {
+  if (!n_out) return fail(PD_ERR_INVALID_ARG, "n_out is NULL");
+  *n_out = 0;
+  if (num_kv_heads < 1 || src_shards < 1 || dst_shards < 1)
+    return fail(PD_ERR_INVALID_ARG, "head and shard counts must be >= 1");
+  if (num_kv_heads % src_shards || num_kv_heads % dst_shards)
+    return fail(PD_ERR_UNSUPPORTED, "both shard counts must divide num_kv_heads (replicated KV heads "
+                                    "are not supported)");
+  const int32_t ps = num_kv_heads / src_shards, pd = num_kv_heads / dst_shards;
+  int32_t k = 0;
+  // source rank s holds heads [s ps, (s + 1) ps), destination rank d holds
+  // [d pd, (d + 1) pd); every overlapping pair is one transfer per page
+  for (int32_t s = 0; s < src_shards; ++s)
+    for (int32_t d = 0; d < dst_shards; ++d) {
+      const int32_t lo = std::max(s * ps, d * pd), hi = std::min((s + 1) * ps, (d + 1) * pd);
+      if (lo >= hi) continue;
+      if (out && k < max_out) out[k] = {s, d, lo - s * ps, hi - s * ps, lo - d * pd, hi - d * pd};
+      ++k;
+    }
+  *n_out = k;
+  if (out && k > max_out) return fail(PD_ERR_WORKSPACE, "out holds fewer than " + std::to_string(k) + " entries");
+  return PD_OK;
+}
+
+pd_status pd_xfer_plan(const pd_attn_desc* desc, int32_t num_layers, void* const* kv_pools,
+                       int32_t num_pool_pages, const int32_t* page_ids, int32_t n, int32_t h0, int32_t h1,
+                       pd_xfer_t* out) {
+  try {
+    if (!out) return fail(PD_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    pd_status s = check_desc(desc);
+    if (s != PD_OK) return s;
+    if ((s = check_heads(desc, h0, h1)) != PD_OK) return s;
+    if (num_layers < 1 || num_layers > kMaxXferLayers)
+      return fail(PD_ERR_INVALID_ARG, "num_layers must be in [1, " + std::to_string(kMaxXferLayers) + "]");
+    if (n < 0) return fail(PD_ERR_INVALID_ARG, "n must be >= 0");
+    if (!kv_pools || (n > 0 && !page_ids)) return fail(PD_ERR_INVALID_ARG, "NULL pointer argument");
+    for (int32_t l = 0; l < num_layers; ++l)
+      if (!kv_pools[l]) return fail(PD_ERR_INVALID_ARG, "pool of layer " + std::to_string(l) + " is NULL");
+    if ((s = check_ids(num_pool_pages, page_ids, n)) != PD_OK) return s;
+    pd_xfer_s* x = new pd_xfer_s;
+    x->desc = *desc;
+    x->L = num_layers;
+    x->n = n;
+    x->h0 = h0;
+    x->h1 = h1;
+    size_t off = 0;
+    x->off_layers = off;
+    off = align_up(off + sizeof(void*) * (size_t)num_layers);
+    x->off_ids = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)n);
+    x->off_done = off;
+    off = align_up(off + sizeof(uint32_t) * (size_t)num_layers);
+    x->ws_bytes = off;
+    x->blob.assign(off, 0);
+    std::memcpy(x->blob.data() + x->off_layers, kv_pools, sizeof(void*) * (size_t)num_layers);
+    if (n) std::memcpy(x->blob.data() + x->off_ids, page_ids, sizeof(int32_t) * (size_t)n);
+    *out = x;
+    return PD_OK;
+  } catch (...) {
+    return fail(PD_ERR_NO_MEMORY, "host allocation failed");
+  }
+}
+
+size_t pd_xfer_buffer_bytes(pd_xfer_t x) {
+  if (!x) return 0;
+  return (size_t)x->L * (size_t)x->n * 2 * (size_t)head_seg_bytes(&x->desc, x->h0, x->h1);
+}
+
+size_t pd_xfer_workspace_bytes(pd_xfer_t x) { return x ? x->ws_bytes : 0; }
+
+pd_status pd_xfer_upload(pd_xfer_t x, void* d_ws, size_t ws_bytes, void* stream) {
+  if (!x || !d_ws) return fail(PD_ERR_INVALID_ARG, "NULL pointer argument");
+  if (ws_bytes < x->ws_bytes) return fail(PD_ERR_WORKSPACE, "workspace smaller than pd_xfer_workspace_bytes");
+  try {
+    return staged_upload(d_ws, x->blob.data(), x->ws_bytes, (hipStream_t)stream);
+  } catch (...) {
+    return fail(PD_ERR_HIP, "unexpected error in upload");
+  }
+}
+
+
+pd_status pd_kv_pack_layers(pd_xfer_t x, void* d_ws, void* d_buf, size_t buf_bytes, uint32_t* progress,
+                            void* stream) {
+  return xfer_layers(x, d_ws, d_buf, buf_bytes, progress, stream, true);
+}
+
+pd_status pd_kv_unpack_layers(pd_xfer_t x, void* d_ws, const void* d_buf, size_t buf_bytes, uint32_t* progress,
+                              void* stream) {
+  return xfer_layers(x, d_ws, d_buf, buf_bytes, progress, stream, false);
+}
+
+void pd_xfer_free(pd_xfer_t x) { delete x; }
 
 const char* pd_status_string(pd_status s) {
   switch (s) {

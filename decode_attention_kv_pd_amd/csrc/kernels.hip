@@ -890,33 +890,59 @@ __global__ __launch_bounds__(kBlockThreads) void append_kernel(AppendParams p) {
 }
 
 // ------------------------------------------------------------------------
-// Page pack / unpack: block (page i, 16 KiB slab), 16-byte copies.
+// Page transfers (pack / unpack, whole pages or a range of KV heads, one or
+// several layers).  Block (page i, 16 KiB slab y, layer l); grid order makes
+// the blocks of layer 0 dispatch first.  The slice of page p moved for
+// layer l is its K part then its V part, each seg_bytes long at seg_off in
+// its half (HND: a head range of a half is one contiguous run); in the
+// buffer it sits at ((l * n + i) * 2 + half) * seg_bytes.
+// With a progress array, the last block of layer l to finish resets that
+// layer's block counter (so the next call starts from zero without a memset)
+// and adds one to progress[l] with a system-scope release store, after every
+// block of the layer has made its copies visible at device scope.
 // ------------------------------------------------------------------------
 constexpr int kPackChunksPerThread = 4;
-__global__ __launch_bounds__(kBlockThreads) void pack_kernel(PackParams p) {
+__global__ __launch_bounds__(kBlockThreads) void xfer_kernel(XferParams p) {
   const int i = blockIdx.x;
+  const int l = blockIdx.z;
   const int64_t page = p.page_ids[i];
-  const int64_t cpp = p.page_bytes / 16;
-  const char* src;
-  char* dst;
-  if (p.to_buffer) {
-    src = (const char*)p.src + page * p.page_bytes;
-    dst = (char*)p.dst + (int64_t)i * p.page_bytes;
-  } else {
-    src = (const char*)p.src + (int64_t)i * p.page_bytes;
-    dst = (char*)p.dst + page * p.page_bytes;
-  }
+  char* pool = (char*)(p.layers ? p.layers[l] : p.pool0);
+  const int64_t segc = p.seg_bytes / 16;
+  char* buf = p.buf + ((int64_t)l * p.n + i) * 2 * p.seg_bytes;
+  char* pg = pool + page * p.page_bytes + p.seg_off;
   const int64_t c0 = (int64_t)blockIdx.y * kBlockThreads * kPackChunksPerThread + threadIdx.x;
   u32x4 v[kPackChunksPerThread];
 #pragma unroll
   for (int k = 0; k < kPackChunksPerThread; ++k) {
     const int64_t c = c0 + k * kBlockThreads;
-    if (c < cpp) v[k] = *(const u32x4*)(src + c * 16);
+    if (c < 2 * segc) {
+      const int64_t pc = c < segc ? c * 16 : p.half_bytes + (c - segc) * 16;
+      v[k] = *(const u32x4*)(p.to_buffer ? pg + pc : buf + c * 16);
+    }
   }
 #pragma unroll
   for (int k = 0; k < kPackChunksPerThread; ++k) {
     const int64_t c = c0 + k * kBlockThreads;
-    if (c < cpp) *(u32x4*)(dst + c * 16) = v[k];
+    if (c < 2 * segc) {
+      const int64_t pc = c < segc ? c * 16 : p.half_bytes + (c - segc) * 16;
+      *(u32x4*)(p.to_buffer ? buf + c * 16 : pg + pc) = v[k];
+    }
+  }
+  if (p.done) {
+    __threadfence();  // this thread's copies, device-wide
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t blocks = gridDim.x * gridDim.y;
+      const uint32_t prev = __hip_atomic_fetch_add(p.done + l, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == blocks - 1) {
+        __hip_atomic_store(p.done + l, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (p.progress) {
+          __threadfence_system();
+          const uint32_t n = __hip_atomic_load(p.progress + l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          __hip_atomic_store(p.progress + l, n + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+      }
+    }
   }
 }
 
@@ -954,12 +980,12 @@ hipError_t launch_append(const AppendParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_pack(const PackParams& p, hipStream_t s) {
-  if (p.n == 0) return hipSuccess;
-  const int64_t cpp = p.page_bytes / 16;
+hipError_t launch_xfer(const XferParams& p, hipStream_t s) {
+  if (p.n == 0 || p.L == 0) return hipSuccess;
+  const int64_t chunks = 2 * p.seg_bytes / 16;
   const int64_t per_block = (int64_t)kBlockThreads * kPackChunksPerThread;
-  const unsigned ny = (unsigned)((cpp + per_block - 1) / per_block);
-  hipLaunchKernelGGL(pack_kernel, dim3(p.n, ny), dim3(kBlockThreads), 0, s, p);
+  const unsigned ny = (unsigned)((chunks + per_block - 1) / per_block);
+  hipLaunchKernelGGL(xfer_kernel, dim3(p.n, ny, p.L), dim3(kBlockThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -77,18 +77,28 @@ struct AppendParams {
   int32_t B, total_rows, H_kv, ps, D, elt;
 };
 
-struct PackParams {
-  void* dst;
-  const void* src;
-  const int32_t* page_ids;  // device
-  int32_t n;
-  int32_t to_buffer;  // 1: pool -> buffer (pack), 0: buffer -> pool (unpack)
-  int64_t page_bytes;
+// Page transfers between a pool (or L layer pools) and a buffer
+// [L][n][2][seg_bytes]: for each listed page, the slice of seg_bytes at
+// seg_off in its K half and in its V half (the whole page when seg_off = 0
+// and seg_bytes = half_bytes).
+struct XferParams {
+  char* buf;
+  void* pool0;               // the pool when layers is null (L = 1)
+  void* const* layers;       // device array of L pool pointers, or null
+  const int32_t* page_ids;   // device, n entries
+  uint32_t* done;            // device, L per-layer block counters (zero between calls), or null
+  uint32_t* progress;        // device-accessible, L per-layer completion counters, or null
+  int64_t page_bytes;        // 2 * half_bytes
+  int64_t half_bytes;        // H_kv * ps * D * elt
+  int64_t seg_off;           // h0 * ps * D * elt
+  int64_t seg_bytes;         // (h1 - h0) * ps * D * elt, a multiple of 16
+  int32_t n, L;
+  int32_t to_buffer;         // 1: pool -> buffer (pack), 0: buffer -> pool (unpack)
 };
 
 hipError_t launch_attention(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_merge(const AttnParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
-hipError_t launch_pack(const PackParams& p, hipStream_t s);
+hipError_t launch_xfer(const XferParams& p, hipStream_t s);
 
 }  // namespace pdk

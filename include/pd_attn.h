@@ -10,6 +10,12 @@
  *                    the merge of split-KV partial results
  *   pd_kv_pack       gather whole pages into one contiguous transfer buffer
  *   pd_kv_unpack     scatter such a buffer into (other) pages
+ *   pd_kv_pack_heads, pd_kv_unpack_heads, pd_kv_shard_transfers
+ *                    the same for a range of KV heads of each page, and the
+ *                    head ranges that move between differently sharded ranks
+ *   pd_xfer_plan, pd_kv_pack_layers, pd_kv_unpack_layers
+ *                    several layers' pages in one launch, with a per-layer
+ *                    completion counter a host thread can poll
  *
  * What the operations compute follows the Perplexity post "Disaggregated
  * prefill and decode" and the kwkr.cn PD-disaggregation survey; each entry
@@ -251,6 +257,139 @@ pd_status pd_kv_unpack(const pd_attn_desc* desc, void* kv_pool,
                        int32_t num_pool_pages, const int32_t* page_ids,
                        int32_t n, const void* d_buf, size_t buf_bytes,
                        void* d_scratch, size_t scratch_bytes, void* stream);
+
+/* ---- Sharded transfers (post, section "Sharded KV Cache Transfers") ----
+ * When the prefiller and the decoder split the KV heads over different
+ * numbers of tensor-parallel ranks, pages are split or rebuilt: each transfer
+ * moves one contiguous range of KV heads of every listed page.  In an HND
+ * page such a range is two contiguous runs, its K part and its V part.  The
+ * pool passed here is one rank's pool (desc->num_kv_heads = that rank's
+ * heads) and [h0, h1) are local head indices of it. */
+
+/* Bytes of the head-[h0, h1) slices of n pages:
+ * n * 2 * (h1 - h0) * page_size * head_dim * element size.  0 on a bad
+ * descriptor, n < 0 or an empty / out-of-range head range. */
+size_t pd_kv_pack_heads_bytes(const pd_attn_desc* desc, int32_t n_pages,
+                              int32_t h0, int32_t h1);
+
+/* Gather KV heads [h0, h1) of the listed pages, in list order, into a
+ * contiguous buffer [n][2][h1 - h0][page_size][head_dim] (K slice then V
+ * slice of each page; bit-exact).  h0 = 0, h1 = num_kv_heads is pd_kv_pack.
+ *   page_ids   HOST array of n page ids in [0, num_pool_pages), no repeats;
+ *              staged through pinned memory to d_scratch on `stream`
+ *   d_buf      device buffer of buf_bytes >= pd_kv_pack_heads_bytes(...)
+ *   d_scratch  device scratch of scratch_bytes >= 4 * n
+ * Errors: PD_ERR_INVALID_ARG (head range not within [0, num_kv_heads) or
+ * empty, NULL pointer, repeated id), PD_ERR_OUT_OF_RANGE, PD_ERR_WORKSPACE,
+ * PD_ERR_UNSUPPORTED, PD_ERR_HIP.  n == 0 is a no-op. */
+pd_status pd_kv_pack_heads(const pd_attn_desc* desc, const void* kv_pool,
+                           int32_t num_pool_pages, const int32_t* page_ids,
+                           int32_t n, int32_t h0, int32_t h1, void* d_buf,
+                           size_t buf_bytes, void* d_scratch,
+                           size_t scratch_bytes, void* stream);
+
+/* Scatter such a buffer into KV heads [h0, h1) of the listed (receiver's)
+ * pages; the page's other heads are not touched, so a full page is rebuilt
+ * from the slices of several senders.  Arguments and errors as
+ * pd_kv_pack_heads. */
+pd_status pd_kv_unpack_heads(const pd_attn_desc* desc, void* kv_pool,
+                             int32_t num_pool_pages, const int32_t* page_ids,
+                             int32_t n, int32_t h0, int32_t h1,
+                             const void* d_buf, size_t buf_bytes,
+                             void* d_scratch, size_t scratch_bytes,
+                             void* stream);
+
+/* One transfer of a sharded handoff: heads [src_h0, src_h1) of the source
+ * rank's pool (local indices) go to heads [dst_h0, dst_h1) of the destination
+ * rank's pool. */
+typedef struct pd_head_transfer {
+  int32_t src_rank, dst_rank;
+  int32_t src_h0, src_h1;
+  int32_t dst_h0, dst_h1;
+} pd_head_transfer;
+
+/* The transfers that move num_kv_heads KV heads, split evenly and in order
+ * (rank r holds heads [r H / S, (r + 1) H / S)) over src_shards prefiller
+ * ranks, to dst_shards decoder ranks: one entry per overlapping (source,
+ * destination) pair, sources in rank order.  A destination page expects one
+ * write per entry naming its rank -- the count the decoder has to know
+ * (s / d "halves" when the prefiller has s = k d ranks, one write when the
+ * decoder has more ranks).  Host only.
+ *   out, max_out   caller array (may be NULL to query the count)
+ *   n_out          number of transfers
+ * Errors: PD_ERR_INVALID_ARG (counts < 1, n_out NULL), PD_ERR_UNSUPPORTED
+ * (a shard count that does not divide num_kv_heads: replicated KV heads),
+ * PD_ERR_WORKSPACE (max_out too small; *n_out still set). */
+pd_status pd_kv_shard_transfers(int32_t num_kv_heads, int32_t src_shards,
+                                int32_t dst_shards, pd_head_transfer* out,
+                                int32_t max_out, int32_t* n_out);
+
+/* ---- Multi-layer transfers with a completion counter ----
+ * The post's section "KV Messenger": copies of a layer's pages start as soon
+ * as that layer's KV has been appended, and a dedicated host thread polls a
+ * counter to learn how far the GPU has got, which keeps the step
+ * graph-capturable.  A transfer plan fixes the L layer pools, the page list
+ * and the head range once (host only); its small table is uploaded to a
+ * caller workspace; each pack then is ONE launch over all L layers, whose
+ * blocks run layer after layer, and each layer bumps its own counter when
+ * its last block has finished.
+ *
+ * Buffer: [L][n][2][h1 - h0][page_size][head_dim] (layer after layer, each
+ * layer as pd_kv_pack_heads).  Progress: NULL, or an array of L uint32 in
+ * pinned host memory (hipHostMalloc, polled by the host) or in device
+ * memory.  Entry l is read and incremented by one (release store at system
+ * scope) once every page of layer l has been copied and made visible; the
+ * library never resets it, so values keep counting across calls and graph
+ * replays (call c of a plan has finished layer l when progress[l] >=
+ * start + c).  The workspace's block counters return to zero at the end of
+ * each call; nothing is cleared with a memset.  Calls that share a workspace
+ * must not overlap. */
+typedef struct pd_xfer_s* pd_xfer_t;
+
+/* Build a transfer plan (host only, no HIP call).
+ *   kv_pools   HOST array of num_layers device pointers, one pool per layer,
+ *              all [num_pool_pages][2][num_kv_heads][page_size][head_dim]
+ *   page_ids   HOST array of n distinct page ids (copied into the plan)
+ *   [h0, h1)   KV heads moved from every page (0, num_kv_heads: whole pages)
+ * Errors: PD_ERR_INVALID_ARG (num_layers not in [1, 4096], NULL pools, bad
+ * head range, repeated id), PD_ERR_OUT_OF_RANGE, PD_ERR_UNSUPPORTED,
+ * PD_ERR_NO_MEMORY. */
+pd_status pd_xfer_plan(const pd_attn_desc* desc, int32_t num_layers,
+                       void* const* kv_pools, int32_t num_pool_pages,
+                       const int32_t* page_ids, int32_t n, int32_t h0,
+                       int32_t h1, pd_xfer_t* out);
+
+/* Bytes of the plan's transfer buffer (0 for a NULL plan). */
+size_t pd_xfer_buffer_bytes(pd_xfer_t xfer);
+
+/* Bytes of device workspace the plan needs (pool pointers, ids, counters). */
+size_t pd_xfer_workspace_bytes(pd_xfer_t xfer);
+
+/* Copy the plan's table into d_ws (async on `stream`, from pinned staging
+ * memory the library owns) and set its block counters to zero.  Do it once,
+ * outside any graph capture, before the first pack / unpack with d_ws.
+ * Errors: PD_ERR_INVALID_ARG, PD_ERR_WORKSPACE, PD_ERR_HIP. */
+pd_status pd_xfer_upload(pd_xfer_t xfer, void* d_ws, size_t ws_bytes,
+                         void* stream);
+
+/* Pack every layer's page slices into d_buf: one launch, no host-to-device
+ * copy, no memset (capturable into a HIP graph).  progress: see above.
+ * Errors: PD_ERR_INVALID_ARG (NULL plan / workspace / buffer, progress that
+ * is neither pinned host nor device memory), PD_ERR_WORKSPACE (buffer too
+ * small), PD_ERR_HIP. */
+pd_status pd_kv_pack_layers(pd_xfer_t xfer, void* d_ws, void* d_buf,
+                            size_t buf_bytes, uint32_t* progress,
+                            void* stream);
+
+/* The inverse on a receiver: write the buffer's slices into the plan's page
+ * ids of every layer pool (the receiver's own ids and pools), heads
+ * [h0, h1) only.  Arguments and errors as pd_kv_pack_layers. */
+pd_status pd_kv_unpack_layers(pd_xfer_t xfer, void* d_ws, const void* d_buf,
+                              size_t buf_bytes, uint32_t* progress,
+                              void* stream);
+
+/* Release a transfer plan (host memory only). */
+void pd_xfer_free(pd_xfer_t xfer);
 
 /* Static text for a status code. */
 const char* pd_status_string(pd_status s);

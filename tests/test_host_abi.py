@@ -133,6 +133,68 @@ def test_pack_unpack_reject_bad_lists_before_device_work():
         expect("PD_ERR_UNSUPPORTED", fn, desc(head_dim=80), pool, 10, [1], buf, scr, stream=0)
 
 
+def test_pack_heads_reject_bad_arguments_before_device_work():
+    d = desc(num_qo_heads=8, num_kv_heads=8)
+    sb = pd.pd_kv_pack_heads_bytes(d, 1, 2, 5)
+    assert sb == 2 * 3 * 16 * 64 * 4
+    pool, buf, scr = FakeTensor(10 * pd.pd_kv_pack_bytes(d, 1)), FakeTensor(2 * sb), FakeTensor(8)
+    for fn in (pd.pd_kv_pack_heads, pd.pd_kv_unpack_heads):
+        for (h0, h1) in [(-1, 2), (3, 3), (5, 4), (0, 9)]:
+            expect("PD_ERR_INVALID_ARG", fn, d, pool, 10, [1], h0, h1, buf, scr, stream=0)
+        expect("PD_ERR_OUT_OF_RANGE", fn, d, pool, 10, [0, 10], 2, 5, buf, scr, stream=0)
+        expect("PD_ERR_INVALID_ARG", fn, d, pool, 10, [3, 3], 2, 5, buf, scr, stream=0)
+        expect("PD_ERR_WORKSPACE", fn, d, pool, 10, [1, 2, 3], 2, 5, buf, scr, stream=0)
+        expect("PD_ERR_WORKSPACE", fn, d, pool, 10, [1, 2], 2, 5, FakeTensor(sb), scr, stream=0)
+        expect("PD_ERR_WORKSPACE", fn, d, pool, 10, [1, 2], 2, 5, buf, FakeTensor(7), stream=0)
+
+
+def test_pack_heads_bytes_formula():
+    d = desc(num_qo_heads=64, num_kv_heads=8, head_dim=128, page_size=64, dtype="bf16")
+    assert pd.pd_kv_pack_heads_bytes(d, 512, 0, 8) == pd.pd_kv_pack_bytes(d, 512)
+    assert pd.pd_kv_pack_heads_bytes(d, 512, 0, 4) == 64 * 2 ** 20
+    assert pd.pd_kv_pack_heads_bytes(d, 3, 7, 8) == 3 * 2 * 64 * 128 * 2
+    assert pd.pd_kv_pack_heads_bytes(d, 3, 4, 4) == 0
+    assert pd.pd_kv_pack_heads_bytes(d, 3, 0, 9) == 0
+
+
+@pytest.mark.parametrize("H,s,d", [(8, 1, 1), (8, 2, 2), (8, 4, 2), (8, 8, 1), (8, 2, 4), (8, 1, 8),
+                                   (6, 2, 3), (6, 3, 2), (64, 8, 2), (1, 1, 1)])
+def test_shard_transfers_match_oracle(H, s, d):
+    from oracle import paged_kv as OP
+    assert pd.pd_kv_shard_transfers(H, s, d) == OP.shard_transfers(H, s, d)
+
+
+def test_shard_transfers_errors():
+    expect("PD_ERR_UNSUPPORTED", pd.pd_kv_shard_transfers, 8, 3, 1)
+    expect("PD_ERR_UNSUPPORTED", pd.pd_kv_shard_transfers, 8, 16, 8)   # replicated heads
+    expect("PD_ERR_INVALID_ARG", pd.pd_kv_shard_transfers, 8, 0, 1)
+    n = pd.ctypes.c_int32(-1)
+    arr = (pd.pd_head_transfer * 1)()
+    st = pd._lib.pd_kv_shard_transfers(8, 4, 2, arr, 1, pd.ctypes.byref(n))
+    assert pd.STATUS[st] == "PD_ERR_WORKSPACE" and n.value == 4
+
+
+def test_xfer_plan_sizes_and_errors():
+    d = desc(num_qo_heads=8, num_kv_heads=8)
+    pools = [0x10000, 0x20000, 0x30000]
+    x = pd.pd_xfer_plan(d, pools, 10, [4, 1, 7], 2, 6)
+    assert x.buffer_bytes == 3 * 3 * 2 * 4 * 16 * 64 * 4
+    assert x.workspace_bytes >= 3 * 8 + 3 * 4 + 3 * 4
+    full = pd.pd_xfer_plan(d, pools, 10, [4, 1, 7])
+    assert full.buffer_bytes == 3 * pd.pd_kv_pack_bytes(d, 3)
+    expect("PD_ERR_INVALID_ARG", pd.pd_xfer_plan, d, [], 10, [1])
+    expect("PD_ERR_INVALID_ARG", pd.pd_xfer_plan, d, [0x1000, 0], 10, [1])
+    expect("PD_ERR_INVALID_ARG", pd.pd_xfer_plan, d, pools, 10, [1], 3, 3)
+    expect("PD_ERR_INVALID_ARG", pd.pd_xfer_plan, d, pools, 10, [1, 1])
+    expect("PD_ERR_OUT_OF_RANGE", pd.pd_xfer_plan, d, pools, 10, [10])
+    expect("PD_ERR_UNSUPPORTED", pd.pd_xfer_plan, desc(head_dim=80), pools, 10, [1])
+    expect("PD_ERR_WORKSPACE", pd.pd_xfer_upload, x, FakeTensor(x.workspace_bytes - 1), stream=0)
+    expect("PD_ERR_WORKSPACE", pd.pd_kv_pack_layers, x, FakeTensor(x.workspace_bytes),
+           FakeTensor(x.buffer_bytes - 1), stream=0)
+    expect("PD_ERR_WORKSPACE", pd.pd_kv_unpack_layers, x, FakeTensor(x.workspace_bytes),
+           FakeTensor(x.buffer_bytes - 1), stream=0)
+
+
 def test_upload_rejects_small_workspace():
     qo, kv, ip, ids, pool = plan_args()
     p = pd.pd_plan(desc(), qo, kv, ip, ids, pool)
