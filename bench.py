@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--phase-reps", type=int, default=5)
     ap.add_argument("--no-phases", action="store_true", help="skip the decode-only / prefill-only legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-transfers", action="store_true",
+                    help="skip the head-range and multi-layer transfer legs")
+    ap.add_argument("--layers", type=int, default=8, help="layers of the multi-layer pack leg")
     ap.add_argument("--cpu-decode-requests", type=int, default=24)
     ap.add_argument("--cpu-prefill-tokens", type=int, default=16)
     return ap.parse_args()
@@ -95,14 +98,14 @@ def measured_traffic(workload):
     were taken (the summary records the source hash)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "attention_long_pmc_traffic.txt")
-    src = os.path.join(ROOT, "decode_attention_kv_pd_amd", "csrc", "kernels.hip")
+    src = os.path.join(ROOT, "decode_attention_kv_pd_amd", "csrc", "attention.hip")
     if workload != "long" or not os.path.exists(path):
         return None
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     for line in open(path):
         if line.startswith("TRAFFIC "):
             kv = dict(t.split("=", 1) for t in line.split()[1:])
-            if kv.get("kernels_sha256_16") == digest:
+            if kv.get("attention_sha256_16") == digest:
                 return int(kv["bytes_per_launch"])
     return None
 
@@ -150,6 +153,81 @@ def cpu_baseline(b, n_dec, n_tok):
                       f"shared by the sampled rows)",
             "seconds": round(secs, 3), "decode_GBps": dec_bytes / secs / 1e9 if n_dec else None,
             "prefill_TFLOPs": pre_flops / secs / 1e12 if n_tok else None}
+
+
+def transfer_legs(args, pd, torch, b, desc, pool, pack_ids, unpack_ids):
+    """Head-range pack / unpack of the chunk request's pages (half of the KV
+    heads: what a rank sends when the decoder has twice the prefiller's TP
+    degree), and a multi-layer pack of the same page count over `--layers`
+    layer pools in one launch, with per-layer progress counters in pinned
+    host memory polled from the host.  Bytes are read + written."""
+    from workloads import device_normal_, device_seed
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    out = {}
+    n = len(pack_ids)
+    h1 = b.H_kv // 2
+    nb = pd.pd_kv_pack_heads_bytes(desc, n, 0, h1)
+    hbuf = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    scr = torch.empty(4 * n, dtype=torch.uint8, device="cuda")
+    pd.pd_kv_pack_heads(desc, pool, b.num_pool_pages, pack_ids, 0, h1, hbuf, scr)
+    t = timed(lambda: pd.pd_kv_pack_heads(desc, pool, b.num_pool_pages, pack_ids, 0, h1, hbuf, scr),
+              args.phase_reps)
+    out["pack_heads"] = {"heads": [0, h1], "pages": n, "bytes": nb, "ms": round(t, 4),
+                         "GBps": round(2 * nb / (t * 1e-3) / 1e9, 1)}
+    t = timed(lambda: pd.pd_kv_unpack_heads(desc, pool, b.num_pool_pages, unpack_ids, 0, h1, hbuf, scr),
+              args.phase_reps)
+    out["unpack_heads"] = {"ms": round(t, 4), "GBps": round(2 * nb / (t * 1e-3) / 1e9, 1)}
+    del hbuf
+
+    L = args.layers
+    P = n + 16
+    pools = [device_normal_(torch.empty((P, 2, b.H_kv, b.ps, b.D), dtype=torch.bfloat16, device="cuda"),
+                            device_seed(b.wid, 1, 10 + layer)) for layer in range(L)]
+    ids = np.random.default_rng(8).permutation(P)[:n].astype(np.int32)
+    x = pd.pd_xfer_plan(desc, pools, P, ids)
+    ws = torch.empty(x.workspace_bytes, dtype=torch.uint8, device="cuda")
+    pd.pd_xfer_upload(x, ws)
+    lbuf = torch.empty(x.buffer_bytes, dtype=torch.uint8, device="cuda")
+    prog = torch.zeros(L, dtype=torch.int32, pin_memory=True)
+    pd.pd_kv_pack_layers(x, ws, lbuf, prog)
+    torch.cuda.synchronize()
+    t = timed(lambda: pd.pd_kv_pack_layers(x, ws, lbuf, prog), args.phase_reps)
+    # the host polls the counters during one more launch (the launch returns
+    # at once; the polling loop runs in this thread, so no lock stands between
+    # the launch and the first read)
+    view = prog.numpy()
+    start = view.copy()
+    flips = [None] * L
+    t_launch = time.perf_counter()
+    pd.pd_kv_pack_layers(x, ws, lbuf, prog)
+    deadline = t_launch + 5.0
+    while any(f is None for f in flips) and time.perf_counter() < deadline:
+        now = time.perf_counter()
+        for layer in range(L):
+            if flips[layer] is None and view[layer] != start[layer]:
+                flips[layer] = now
+    torch.cuda.synchronize()
+    t_sync = time.perf_counter()
+    ready = [round((f - t_launch) * 1e6, 1) if f is not None else None for f in flips]
+    out["pack_layers"] = {"layers": L, "pages_per_layer": n, "bytes": x.buffer_bytes, "ms": round(t, 4),
+                          "GBps": round(2 * x.buffer_bytes / (t * 1e-3) / 1e9, 1),
+                          "host_seen_layer_ready_us": ready,
+                          "host_launch_to_sync_us": round((t_sync - t_launch) * 1e6, 1)}
+    x.close()
+    del pools, lbuf
+    torch.cuda.synchronize()
+    return out
 
 
 def main():
@@ -327,6 +405,10 @@ def main():
         result["decode_attn_GBps"] = legs["decode_only"]["GBps"]
         result["prefill_attn_TFLOPs"] = legs["prefill_only"]["TFLOPs"]
         print(f"[bench] phase legs done", file=sys.stderr, flush=True)
+
+    if not args.no_transfers:
+        result["transfers"] = transfer_legs(args, pd, torch, b, desc, pool, pack_ids, unpack_ids)
+        print(f"[bench] transfer legs done", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)

@@ -1,6 +1,6 @@
-// HIP kernels for gfx950 (MI355X, CDNA4): KV append, page pack/unpack,
-// ragged paged attention (causal prefill tiles on bf16 MFMA and split-KV
-// decode units in one launch), and the merge of split-KV partial results.
+// HIP attention kernels for gfx950 (MI355X, CDNA4): ragged paged attention
+// (causal prefill tiles on bf16 MFMA and split-KV decode units in one
+// launch), the fp32 variant, and the merge of split-KV partial results.
 //
 // What is computed follows the Perplexity post "Disaggregated prefill and
 // decode": requests with many query tokens (prefill, compute bound) and
@@ -859,93 +859,6 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(AttnParams p) {
   }
 }
 
-// ------------------------------------------------------------------------
-// KV append: one block per new token row; 16-byte copies of each head's K
-// and V row into (page, slot) of position kv - qo + i.
-// ------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlockThreads) void append_kernel(AppendParams p) {
-  const int row = blockIdx.x;
-  int lo = 0, hi = p.B - 1;  // last request with qo_indptr[r] <= row
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (ldc(p.qo_indptr + mid) <= row) lo = mid; else hi = mid - 1;
-  }
-  const ReqInfo ri = ldc(p.req + lo);
-  const int pos = ri.kv - ri.qo + (row - ri.qo_start);
-  const int page = ldc(p.page_indices + ri.page_start + pos / p.ps);
-  const int slot = pos % p.ps;
-  const int64_t head_bytes = (int64_t)p.D * p.elt;
-  const int cph = (int)(head_bytes / 16);
-  const int64_t page_bytes = 2 * (int64_t)p.H_kv * p.ps * head_bytes;
-  char* pool = (char*)p.pool + (int64_t)page * page_bytes;
-  const int total = 2 * p.H_kv * cph;
-  for (int c = threadIdx.x; c < total; c += kBlockThreads) {
-    const int kvsel = c / (p.H_kv * cph);
-    const int hh = (c / cph) % p.H_kv;
-    const int cc = c % cph;
-    const char* src = (const char*)(kvsel ? p.v_new : p.k_new) + ((int64_t)row * p.H_kv + hh) * head_bytes + cc * 16;
-    char* dst = pool + (((int64_t)kvsel * p.H_kv + hh) * p.ps + slot) * head_bytes + cc * 16;
-    *(u32x4*)dst = *(const u32x4*)src;
-  }
-}
-
-// ------------------------------------------------------------------------
-// Page transfers (pack / unpack, whole pages or a range of KV heads, one or
-// several layers).  Block (page i, 16 KiB slab y, layer l); grid order makes
-// the blocks of layer 0 dispatch first.  The slice of page p moved for
-// layer l is its K part then its V part, each seg_bytes long at seg_off in
-// its half (HND: a head range of a half is one contiguous run); in the
-// buffer it sits at ((l * n + i) * 2 + half) * seg_bytes.
-// With a progress array, the last block of layer l to finish resets that
-// layer's block counter (so the next call starts from zero without a memset)
-// and adds one to progress[l] with a system-scope release store, after every
-// block of the layer has made its copies visible at device scope.
-// ------------------------------------------------------------------------
-constexpr int kPackChunksPerThread = 4;
-__global__ __launch_bounds__(kBlockThreads) void xfer_kernel(XferParams p) {
-  const int i = blockIdx.x;
-  const int l = blockIdx.z;
-  const int64_t page = p.page_ids[i];
-  char* pool = (char*)(p.layers ? p.layers[l] : p.pool0);
-  const int64_t segc = p.seg_bytes / 16;
-  char* buf = p.buf + ((int64_t)l * p.n + i) * 2 * p.seg_bytes;
-  char* pg = pool + page * p.page_bytes + p.seg_off;
-  const int64_t c0 = (int64_t)blockIdx.y * kBlockThreads * kPackChunksPerThread + threadIdx.x;
-  u32x4 v[kPackChunksPerThread];
-#pragma unroll
-  for (int k = 0; k < kPackChunksPerThread; ++k) {
-    const int64_t c = c0 + k * kBlockThreads;
-    if (c < 2 * segc) {
-      const int64_t pc = c < segc ? c * 16 : p.half_bytes + (c - segc) * 16;
-      v[k] = *(const u32x4*)(p.to_buffer ? pg + pc : buf + c * 16);
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < kPackChunksPerThread; ++k) {
-    const int64_t c = c0 + k * kBlockThreads;
-    if (c < 2 * segc) {
-      const int64_t pc = c < segc ? c * 16 : p.half_bytes + (c - segc) * 16;
-      *(u32x4*)(p.to_buffer ? buf + c * 16 : pg + pc) = v[k];
-    }
-  }
-  if (p.done) {
-    __threadfence();  // this thread's copies, device-wide
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t blocks = gridDim.x * gridDim.y;
-      const uint32_t prev = __hip_atomic_fetch_add(p.done + l, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == blocks - 1) {
-        __hip_atomic_store(p.done + l, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (p.progress) {
-          __threadfence_system();
-          const uint32_t n = __hip_atomic_load(p.progress + l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-          __hip_atomic_store(p.progress + l, n + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-        }
-      }
-    }
-  }
-}
-
 }  // namespace
 
 hipError_t launch_attention(const AttnParams& p, int dtype, hipStream_t s) {
@@ -971,21 +884,6 @@ hipError_t launch_merge(const AttnParams& p, hipStream_t s) {
     hipLaunchKernelGGL(merge_kernel<128>, dim3(p.n_mg), dim3(kBlockThreads), 0, s, p);
   else
     hipLaunchKernelGGL(merge_kernel<64>, dim3(p.n_mg), dim3(kBlockThreads), 0, s, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_append(const AppendParams& p, hipStream_t s) {
-  if (p.total_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(append_kernel, dim3(p.total_rows), dim3(kBlockThreads), 0, s, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_xfer(const XferParams& p, hipStream_t s) {
-  if (p.n == 0 || p.L == 0) return hipSuccess;
-  const int64_t chunks = 2 * p.seg_bytes / 16;
-  const int64_t per_block = (int64_t)kBlockThreads * kPackChunksPerThread;
-  const unsigned ny = (unsigned)((chunks + per_block - 1) / per_block);
-  hipLaunchKernelGGL(xfer_kernel, dim3(p.n, ny, p.L), dim3(kBlockThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -1,0 +1,161 @@
+// HIP KV-cache copy kernels for gfx950 (MI355X, CDNA4): the append of new
+// K/V rows into their pages, and page transfers (pack / unpack of whole pages
+// or of a range of KV heads, for one or several layers, with per-layer
+// completion counters).
+//
+// What is copied follows the Perplexity post "Disaggregated prefill and
+// decode": K/V are appended to the paged cache before attention reads them
+// and copies of a layer's pages may start right after its append (section
+// "KV Messenger"); pages hold heads before tokens, so a page and each head
+// range of it are contiguous runs, and differently sharded ranks exchange
+// head ranges of pages (section "Sharded KV Cache Transfers").  Every copy is
+// bit-exact (16-byte moves of the stored bytes).
+//
+// Layout recap (see include/pd_attn.h): pool [pages][2][H_kv][ps][D],
+// k_new / v_new [rows][H_kv][D].
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pd_internal.hpp"
+
+namespace pdk {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Planner tables are read through the constant address space (wave-uniform
+// reads become scalar loads).
+#define CONST_AS __attribute__((address_space(4)))
+template <class T>
+__device__ __forceinline__ T ldc(const T* p) {
+  static_assert(sizeof(T) % 4 == 0, "dword-sized tables");
+  T out;
+  const CONST_AS int32_t* src = (const CONST_AS int32_t*)p;
+  int32_t* dst = (int32_t*)&out;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) dst[i] = src[i];
+  return out;
+}
+
+// ------------------------------------------------------------------------
+// KV append: one block per new token row; 16-byte copies of each head's K
+// and V row into (page, slot) of position kv - qo + i.
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlockThreads) void append_kernel(AppendParams p) {
+  const int row = blockIdx.x;
+  int lo = 0, hi = p.B - 1;  // last request with qo_indptr[r] <= row
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ldc(p.qo_indptr + mid) <= row) lo = mid; else hi = mid - 1;
+  }
+  const ReqInfo ri = ldc(p.req + lo);
+  const int pos = ri.kv - ri.qo + (row - ri.qo_start);
+  const int page = ldc(p.page_indices + ri.page_start + pos / p.ps);
+  const int slot = pos % p.ps;
+  const int64_t head_bytes = (int64_t)p.D * p.elt;
+  const int cph = (int)(head_bytes / 16);
+  const int64_t page_bytes = 2 * (int64_t)p.H_kv * p.ps * head_bytes;
+  char* pool = (char*)p.pool + (int64_t)page * page_bytes;
+  const int total = 2 * p.H_kv * cph;
+  for (int c = threadIdx.x; c < total; c += kBlockThreads) {
+    const int kvsel = c / (p.H_kv * cph);
+    const int hh = (c / cph) % p.H_kv;
+    const int cc = c % cph;
+    const char* src = (const char*)(kvsel ? p.v_new : p.k_new) + ((int64_t)row * p.H_kv + hh) * head_bytes + cc * 16;
+    char* dst = pool + (((int64_t)kvsel * p.H_kv + hh) * p.ps + slot) * head_bytes + cc * 16;
+    *(u32x4*)dst = *(const u32x4*)src;
+  }
+}
+
+// ------------------------------------------------------------------------
+// Page transfers (pack / unpack, whole pages or a range of KV heads, one or
+// several layers).  Block (page i, 16 KiB slab y, layer l); grid order makes
+// the blocks of layer 0 dispatch first.  The slice of page p moved for
+// layer l is its K part then its V part, each seg_bytes long at seg_off in
+// its half (HND: a head range of a half is one contiguous run); in the
+// buffer it sits at ((l * n + i) * 2 + half) * seg_bytes.
+// With a progress array the copies are written through to memory (stores
+// coherent at system scope, so no L2 write-back is needed to publish them),
+// each block counts itself done once its stores are acknowledged, and the
+// last block of layer l to finish resets that layer's block counter (so the
+// next call starts from zero without a memset) and adds one to progress[l]
+// with a system-scope release store.
+// ------------------------------------------------------------------------
+constexpr int kPackChunksPerThread = 4;
+
+// 16-byte vector store written through to memory (coherent at system scope).
+__device__ __forceinline__ void store16_sys(char* p, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
+}
+
+__global__ __launch_bounds__(kBlockThreads) void xfer_kernel(XferParams p) {
+  const int i = blockIdx.x;
+  const int l = blockIdx.z;
+  const int64_t page = p.page_ids[i];
+  char* pool = (char*)(p.layers ? p.layers[l] : p.pool0);
+  const int64_t segc = p.seg_bytes / 16;
+  char* buf = p.buf + ((int64_t)l * p.n + i) * 2 * p.seg_bytes;
+  char* pg = pool + page * p.page_bytes + p.seg_off;
+  const int64_t c0 = (int64_t)blockIdx.y * kBlockThreads * kPackChunksPerThread + threadIdx.x;
+  u32x4 v[kPackChunksPerThread];
+#pragma unroll
+  for (int k = 0; k < kPackChunksPerThread; ++k) {
+    const int64_t c = c0 + k * kBlockThreads;
+    if (c < 2 * segc) {
+      const int64_t pc = c < segc ? c * 16 : p.half_bytes + (c - segc) * 16;
+      v[k] = *(const u32x4*)(p.to_buffer ? pg + pc : buf + c * 16);
+    }
+  }
+  if (!p.done) {
+#pragma unroll
+    for (int k = 0; k < kPackChunksPerThread; ++k) {
+      const int64_t c = c0 + k * kBlockThreads;
+      if (c < 2 * segc) {
+        const int64_t pc = c < segc ? c * 16 : p.half_bytes + (c - segc) * 16;
+        *(u32x4*)(p.to_buffer ? buf + c * 16 : pg + pc) = v[k];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kPackChunksPerThread; ++k) {
+      const int64_t c = c0 + k * kBlockThreads;
+      if (c < 2 * segc) {
+        const int64_t pc = c < segc ? c * 16 : p.half_bytes + (c - segc) * 16;
+        store16_sys(p.to_buffer ? buf + c * 16 : pg + pc, v[k]);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have reached memory
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t blocks = gridDim.x * gridDim.y;
+      const uint32_t prev = __hip_atomic_fetch_add(p.done + l, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == blocks - 1) {
+        __hip_atomic_store(p.done + l, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (p.progress) {
+          __threadfence_system();
+          const uint32_t n = __hip_atomic_load(p.progress + l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          __hip_atomic_store(p.progress + l, n + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& p, hipStream_t s) {
+  if (p.total_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(append_kernel, dim3(p.total_rows), dim3(kBlockThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_xfer(const XferParams& p, hipStream_t s) {
+  if (p.n == 0 || p.L == 0) return hipSuccess;
+  const int64_t chunks = 2 * p.seg_bytes / 16;
+  const int64_t per_block = (int64_t)kBlockThreads * kPackChunksPerThread;
+  const unsigned ny = (unsigned)((chunks + per_block - 1) / per_block);
+  hipLaunchKernelGGL(xfer_kernel, dim3(p.n, ny, p.L), dim3(kBlockThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace pdk
