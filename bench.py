@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--no-transfers", action="store_true",
                     help="skip the head-range and multi-layer transfer legs")
     ap.add_argument("--layers", type=int, default=8, help="layers of the multi-layer pack leg")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the interference / chunked-prefill sweep")
+    ap.add_argument("--sweep-decodes", type=int, default=32, help="decodes in the 1PnD sweep batches")
     ap.add_argument("--cpu-decode-requests", type=int, default=24)
     ap.add_argument("--cpu-prefill-tokens", type=int, default=16)
     return ap.parse_args()
@@ -228,6 +231,91 @@ def transfer_legs(args, pd, torch, b, desc, pool, pack_ids, unpack_ids):
     del pools, lbuf
     torch.cuda.synchronize()
     return out
+
+
+def interference_sweep(args, pd, torch):
+    """Kernel-level analogue of the interference comparison in the kwkr.cn
+    survey, section 2 (one prefill batched with n decodes, "1PnD", against the
+    n decodes alone, "nD", and the prefill alone), over prompt lengths, and of
+    its section 8 remark that every chunk of a chunked prefill re-reads all
+    earlier KV.  Shapes of the mixed workload (H 32/8, D 128, page 16, bf16);
+    each decode's cache holds as many tokens as the prompt.  Times are the
+    attention launch + merge, averaged over back-to-back launches."""
+    from workloads import device_normal_, device_seed, make_batch
+
+    reps = 20
+
+    def per_launch(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def setup(b, qo, kv, page_indptr, page_indices):
+        desc = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype, b.causal, b.sm_scale)
+        plan = pd.pd_plan(desc, qo, kv, page_indptr, page_indices, b.num_pool_pages)
+        ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+        pd.pd_plan_upload(plan, ws)
+        rows = max(int(np.sum(qo)), 1)
+        q = device_normal_(torch.empty((rows, b.H_q, b.D), dtype=torch.bfloat16, device="cuda"), 5)
+        o = torch.empty((rows, b.H_q, b.D), dtype=torch.float32, device="cuda")
+        lse = torch.empty((rows, b.H_q), dtype=torch.float32, device="cuda")
+        return plan, ws, q, o, lse
+
+    n = args.sweep_decodes
+    res = {"shapes": "H 32/8, D 128, page 16, bf16; decode caches as long as the prompt",
+           "decodes": n, "points": [], "chunked": []}
+    for L in (128, 256, 512, 1024, 2048, 4096):
+        qo = np.array([L] + [1] * n, np.int32)
+        kv = np.array([L] * (n + 1), np.int32)
+        b = make_batch("mixed", lengths=(qo, kv), materialize=False)
+        pool = device_normal_(torch.empty(b.pool_shape, dtype=torch.bfloat16, device="cuda"), device_seed(4, L, 0))
+        pt = {"prompt": L}
+        for name, sel in (("1PnD", qo), ("nD", np.array([0] + [1] * n, np.int32)),
+                          ("prefill_only", np.array([L] + [0] * n, np.int32))):
+            plan, ws, q, o, lse = setup(b, sel, kv, b.page_indptr, b.page_indices)
+            pt[name + "_us"] = round(per_launch(lambda: pd.pd_attention_run(plan, ws, q, pool, o, lse)) * 1e3, 2)
+            plan.close()
+        pt["ratio_vs_nD"] = round(pt["1PnD_us"] / pt["nD_us"], 3)
+        pt["ratio_vs_sum"] = round(pt["1PnD_us"] / (pt["nD_us"] + pt["prefill_only_us"]), 3)
+        res["points"].append(pt)
+        del pool
+    # chunked prefill of one 4096-token prompt: chunk c attends over the
+    # c + 1 chunks' keys (all earlier KV re-read)
+    P = 4096
+    b = make_batch("mixed", lengths=([P], [P]), materialize=False)
+    pool = device_normal_(torch.empty(b.pool_shape, dtype=torch.bfloat16, device="cuda"), device_seed(4, 0, 1))
+    kv_token_bytes = 2 * b.H_kv * b.D * 2
+    for C in (256, 512, 1024, 2048, 4096):
+        legs = []
+        for c in range(P // C):
+            kv_c = (c + 1) * C
+            npg = -(-kv_c // b.ps)
+            legs.append(setup(b, np.array([C], np.int32), np.array([kv_c], np.int32),
+                              np.array([0, npg], np.int32), np.asarray(b.page_indices[:npg])))
+
+        def run_all():
+            for (plan, ws, q, o, lse) in legs:
+                pd.pd_attention_run(plan, ws, q, pool, o, lse)
+
+        t = per_launch(run_all)
+        res["chunked"].append({"prompt": P, "chunk": C, "launches": len(legs), "us": round(t * 1e3, 2),
+                               "kv_bytes_read": sum((c + 1) * C for c in range(P // C)) * kv_token_bytes})
+        for leg in legs:
+            leg[0].close()
+    single = res["chunked"][-1]["us"]
+    for r in res["chunked"]:
+        r["time_vs_single"] = round(r["us"] / single, 3)
+        r["kv_reread_factor"] = round(r["kv_bytes_read"] / (P * kv_token_bytes), 2)
+    del pool
+    torch.cuda.synchronize()
+    return res
 
 
 def main():
@@ -409,6 +497,10 @@ def main():
     if not args.no_transfers:
         result["transfers"] = transfer_legs(args, pd, torch, b, desc, pool, pack_ids, unpack_ids)
         print(f"[bench] transfer legs done", file=sys.stderr, flush=True)
+
+    if not args.no_sweep:
+        result["interference_sweep"] = interference_sweep(args, pd, torch)
+        print(f"[bench] interference sweep done", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)

@@ -136,3 +136,23 @@ def test_chunked_prefill_equals_full():
     O, _ = oracle_outputs(full)
     assert np.abs(got - O).max() <= tolerance(full)
     assert np.abs(got - out_f).max() <= 2 * tolerance(full)
+
+
+@pytest.mark.parametrize("L", [128, 1024])
+def test_interference_sweep_batches(L):
+    """The interference sweep's 1PnD batch (one causal prompt of L tokens
+    plus decodes over caches of L tokens, the mixed workload's shapes) at
+    parity, and its decode-only / prefill-only halves equal to the mixed
+    launch's rows (kwkr.cn survey, section 2)."""
+    n = 8
+    qo, kv = [L] + [1] * n, [L] * (n + 1)
+    b = make_batch("mixed", lengths=(qo, kv))
+    out_m, lse_m = check(b, f"sweep{L}")
+    for keep in ("decode", "prefill"):
+        sel = np.array([keep == "prefill"] + [keep == "decode"] * n)
+        part = make_batch("mixed", lengths=(list(np.where(sel, qo, 0)), kv))
+        part.q = b.q[np.repeat(sel, qo)].copy()
+        part.k, part.v = b.k, b.v
+        out_p, _ = DeviceRun(part).step()
+        rows = np.repeat(sel, qo)
+        assert np.abs(out_p - out_m[rows]).max() <= 2 * tolerance(b)
