@@ -74,10 +74,18 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const LDS_AS char* p) {
 
 __device__ __forceinline__ u32x4 lds_read16(const LDS_AS char* p) { return *(const LDS_AS u32x4*)p; }
 
-// 16 bytes per lane, global -> LDS without passing through VGPRs.  `lds` is
-// the wave-uniform base of a 1 KiB destination; lane i lands at lds + 16 * i.
+// 16 bytes per lane, global -> LDS without passing through VGPRs
+// (global_load_lds_dwordx4).  `lds` is the wave-uniform base of a 1 KiB
+// destination, passed in M0; lane i lands at lds + 16 * i.
+// Issued from inline asm: the compiler's own wait insertion treats every LDS
+// read that follows a direct-to-LDS load as possibly aliasing it and waits
+// for all loads in flight (vmcnt(0)), which would wait for the prefetches of
+// later tiles too.  The kernels instead wait for exactly the loads they need
+// (s_waitcnt vmcnt(n) before the barrier that publishes a tile).  The s_nop
+// is the wait state a write of M0 needs before a direct-to-LDS load reads it.
 __device__ __forceinline__ void load_lds16(const void* src, LDS_AS char* lds) {
-  __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)lds, 16, 0, 0);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
 
 // Reductions across lane l and lane l ^ 32 / l ^ 16 (v_permlane*_swap).
@@ -120,9 +128,10 @@ __device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballo
 // rescaled and P recomputed.  m_ref never exceeds the true running maximum,
 // so P never underflows more than with an exact maximum, and P < 2^64 stays
 // far inside the bf16 / fp32 range.  The normaliser l is the sum of the same
-// bf16-rounded P that multiply V (an extra MFMA against an all-ones operand),
-// so O is an exact convex combination of V rows whatever m_ref is, and a
-// single dominant key is reproduced exactly.
+// bf16-rounded P that multiply V (v_dot2 against bf16 ones in the prefill
+// role, an extra MFMA against an all-ones operand in the decode role), so O
+// is a convex combination of V rows whatever m_ref is, and a single dominant
+// key is reproduced exactly.
 
 // LDS tile layout (K and V tiles of the prefill role, V stages of the decode
 // role).  Rows of D bf16 go into 1 KiB load blocks of RPB = 512 / D rows,
@@ -404,13 +413,15 @@ __device__ void decode_unit(const AttnParams& p, int unit, LDS_AS char* lds) {
 //   Wave w owns query rows 32 w .. 32 w + 31 (the N index of both products).
 //   S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16; Q^T stays in
 //   registers; K and V tiles are staged in LDS by direct global->LDS loads
-//   (three tiles in flight, each wave loading one 8-row group), read back 16
+//   (four buffers of each, each wave loading one 8-row group), read back 16
 //   bytes per lane (K) and transposed (V); P^T is the S accumulator re-packed
-//   to bf16 in place.  Eight wavefronts share every K/V tile: the tile stream
-//   from L2 is what bounds this role, so rows per tile are what pays.  The
-//   loop is software-pipelined: S of tile t + 1 runs on the MFMA pipe while
-//   the VALU computes the softmax of tile t, then PV of tile t.  Tiles that
-//   cross the causal diagonal (or the end of the cache) run a masked copy.
+//   to bf16 in place, and the row sums of the rounded P are v_dot2 sums.
+//   Eight wavefronts share every K/V tile.  The loop is software-pipelined:
+//   S of tile t + 1 runs on the MFMA pipe while the VALU computes the
+//   softmax of tile t, then PV of tile t; the workgroup meets at a barrier
+//   once per pair of tiles, so the two wavefronts of a SIMD need not run the
+//   same phase at the same time.  Tiles that cross the causal diagonal (or
+//   the end of the cache) run a masked copy.
 // ------------------------------------------------------------------------
 template <int D>
 struct PrefillCfg {
@@ -419,7 +430,7 @@ struct PrefillCfg {
   static constexpr int RPB = Lds<D>::RPB;
   static constexpr int ROWS_PER_WAVE = 64 / kAttnWaves;  // K/V rows each wave loads per tile
   static constexpr int LOADS = ROWS_PER_WAVE / RPB;      // 1 KiB loads per wave per matrix per tile
-  static constexpr int NBUF = 3;                         // K and V tiles in flight
+  static constexpr int NBUF = 4;                         // K and V tile buffers (tile t in buffer t % 4)
   static constexpr int TILE_BYTES = Lds<D>::bytes(64);
   static constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
 };
@@ -508,7 +519,7 @@ __device__ __forceinline__ void prefill_scores(const LDS_AS char* kt, PrefillLan
 // P in bf16 pairs, in the key order of the PV operand (pk[kb][4 sp + i]).
 template <int D, bool MASK>
 __device__ __forceinline__ void prefill_softmax(const AttnParams& p, f32x16 (&s)[2], int kbase, int lim,
-                                                PrefillLanes ln, float& m_ref, f32x16& lacc,
+                                                PrefillLanes ln, float& m_ref, float& lsum,
                                                 f32x16 (&oacc)[D / 32], uint32_t (&pk)[2][8]) {
   using C = PrefillCfg<D>;
   const float cl = p.c_log2;
@@ -537,7 +548,7 @@ __device__ __forceinline__ void prefill_softmax(const AttnParams& p, f32x16 (&s)
     mx = max_x32(mx);
     const float m_new = fmaxf(m_ref, mx);
     const float alpha = fast_exp2((m_ref - m_new) * cl);  // m_ref = -inf -> 0
-    lacc = lacc * alpha;
+    lsum *= alpha;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) oacc[db] = oacc[db] * alpha;
     m_ref = m_new;
@@ -551,11 +562,10 @@ __device__ __forceinline__ void prefill_softmax(const AttnParams& p, f32x16 (&s)
   }
 }
 
-// O^T += V^T P^T over the four 16-key k-steps of one tile (and the row sums of
-// the bf16 P into lacc).
+// O^T += V^T P^T over the four 16-key k-steps of one tile.
 template <int D>
 __device__ __forceinline__ void prefill_pv(const LDS_AS char* vt, PrefillLanes ln, const uint32_t (&pk)[2][8],
-                                           f32x16& lacc, f32x16 (&oacc)[D / 32]) {
+                                           f32x16 (&oacc)[D / 32]) {
   using C = PrefillCfg<D>;
   constexpr int RPB = C::RPB;
 #pragma unroll
@@ -563,7 +573,6 @@ __device__ __forceinline__ void prefill_pv(const LDS_AS char* vt, PrefillLanes l
 #pragma unroll
     for (int sp = 0; sp < 2; ++sp) {
       const u32x4 pb = {pk[kb][4 * sp + 0], pk[kb][4 * sp + 1], pk[kb][4 * sp + 2], pk[kb][4 * sp + 3]};
-      lacc = mfma32(u32x4{kBf16OnesPair, kBf16OnesPair, kBf16OnesPair, kBf16OnesPair}, pb, lacc);
       const LDS_AS char* vp = vt + ln.v_off + ((32 * kb + 16 * sp) / RPB) * Lds<D>::BLOCK;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
@@ -575,58 +584,62 @@ __device__ __forceinline__ void prefill_pv(const LDS_AS char* vt, PrefillLanes l
     }
 }
 
-// s_waitcnt vmcnt(n) for n in {0, L, 2L} (the count must be an immediate).
-template <int L>
-__device__ __forceinline__ void wait_vm(int n) {
-  if (n >= 2 * L) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L) : "memory");
-  else if (n >= L) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 struct PrefillLoop {
   int ntiles, nfull;
-  int pg_k, pg_v;  // page ids of the next K and V loads (scalar loads one iteration ahead)
-  int slot;        // t % NBUF
+  int pg[3];  // page ids of tiles t + 2, t + 3, t + 4 for the loads issued at the next even t
 };
 
-// One pipelined iteration t.  Issue order of the loads is K(t+3), V(t+2) per
-// iteration (K(0) V(0) K(1) V(1) K(2) before the loop), so at the top of
-// iteration t K(t+1) and V(t) are complete once at most the loads of
-// iteration t - 1 (K(t+2), V(t+1)) are outstanding.  Then S(t+1) on the MFMA
-// pipe, the softmax of S(t) on the VALU, and PV(t).
+// One pipelined iteration t over the 64-key tile t (K and V tiles live in
+// buffer t % 4).  The workgroup synchronises once per pair of tiles: at even
+// t every wave waits for its loads of the pair issued at t - 2 (K(t+1),
+// K(t+2), V(t), V(t+1): all it has in flight), the barrier publishes them,
+// and the wave issues its part of K(t+3), K(t+4), V(t+2), V(t+3) into the
+// buffers of tiles t - 1 and t, which every wave finished reading before
+// that barrier.  Between barriers the two wavefronts that share a SIMD can
+// drift apart by up to a tile, so one's softmax overlaps the other's
+// matrix products.  Then S(t+1) on the MFMA pipe, the softmax of S(t) on the
+// VALU, and PV(t).
 template <int D, bool MASK, bool NEXT>
 __device__ __forceinline__ void prefill_iter(const AttnParams& p, const ReqInfo& ri, const PrefillItem& it,
                                              int t, int w, int lane, bool active, int lim, PrefillLanes ln,
                                              const u32x4 (&qf)[D / 16], LDS_AS char* kbuf, LDS_AS char* vbuf,
-                                             PrefillLoop& L, f32x16 (&s_cur)[2], float& m_ref, f32x16& lacc,
-                                             f32x16 (&oacc)[D / 32]) {
+                                             PrefillLoop& L, f32x16 (&s_cur)[2], f32x16 (&s_next)[2],
+                                             float& m_ref, float& lsum, f32x16 (&oacc)[D / 32]) {
   using C = PrefillCfg<D>;
+  static_assert(C::NBUF == 4, "two tiles per barrier with one pair in flight");
   const int nt = L.ntiles;
-  wait_vm<C::LOADS>(C::LOADS * ((t + 1 < nt) + (t + 2 < nt)));
-  __syncthreads();
-  const int s0 = L.slot, s1 = s0 == C::NBUF - 1 ? 0 : s0 + 1, s2 = s1 == C::NBUF - 1 ? 0 : s1 + 1;
-  if (t + 3 < nt) {
-    prefill_issue_k<D>(p, it.hk, it.kv_end, (t + 3) * 64, w, L.pg_k, lane, t + 3 < L.nfull,
-                       kbuf + s0 * C::TILE_BYTES);
-    L.pg_k = prefill_page<D>(p, ri, it.kv_end, (t + 4) * 64, w);
-  }
-  if (t + 2 < nt) {
-    prefill_issue_v<D>(p, it.hk, it.kv_end, (t + 2) * 64, w, L.pg_v, lane, t + 2 < L.nfull,
-                       vbuf + s2 * C::TILE_BYTES);
-    L.pg_v = prefill_page<D>(p, ri, it.kv_end, (t + 3) * 64, w);
+  if ((t & 1) == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 2 < nt)
+      prefill_issue_v<D>(p, it.hk, it.kv_end, (t + 2) * 64, w, L.pg[0], lane, t + 2 < L.nfull,
+                         vbuf + ((t + 2) & 3) * C::TILE_BYTES);
+    if (t + 3 < nt) {
+      prefill_issue_k<D>(p, it.hk, it.kv_end, (t + 3) * 64, w, L.pg[1], lane, t + 3 < L.nfull,
+                         kbuf + ((t + 3) & 3) * C::TILE_BYTES);
+      prefill_issue_v<D>(p, it.hk, it.kv_end, (t + 3) * 64, w, L.pg[1], lane, t + 3 < L.nfull,
+                         vbuf + ((t + 3) & 3) * C::TILE_BYTES);
+    }
+    if (t + 4 < nt)
+      prefill_issue_k<D>(p, it.hk, it.kv_end, (t + 4) * 64, w, L.pg[2], lane, t + 4 < L.nfull,
+                         kbuf + (t & 3) * C::TILE_BYTES);
+  } else {
+    // page ids for the loads of the next even iteration t + 1 (scalar loads)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) L.pg[j] = prefill_page<D>(p, ri, it.kv_end, (t + 3 + j) * 64, w);
   }
   if (active) {
-    f32x16 s_next[2];
-    if (NEXT) prefill_scores<D>(kbuf + s1 * C::TILE_BYTES, ln, qf, s_next);  // NEXT: t + 1 < ntiles
+    if (NEXT) prefill_scores<D>(kbuf + ((t + 1) & 3) * C::TILE_BYTES, ln, qf, s_next);  // NEXT: t + 1 < ntiles
     uint32_t pk[2][8];
-    prefill_softmax<D, MASK>(p, s_cur, t * 64, lim, ln, m_ref, lacc, oacc, pk);
-    prefill_pv<D>(vbuf + s0 * C::TILE_BYTES, ln, pk, lacc, oacc);
-    if (NEXT) {
-      s_cur[0] = s_next[0];
-      s_cur[1] = s_next[1];
-    }
+    prefill_softmax<D, MASK>(p, s_cur, t * 64, lim, ln, m_ref, lsum, oacc, pk);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[kb][i]),
+                                               __builtin_bit_cast(bf16x2, kBf16OnesPair), lsum, false);
+    prefill_pv<D>(vbuf + (t & 3) * C::TILE_BYTES, ln, pk, oacc);
   }
-  L.slot = s1;
 }
 
 template <int D>
@@ -670,18 +683,18 @@ __device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
   float m_ref = -INFINITY;
-  f32x16 lacc = {};  // row sums of the bf16 P (all sixteen entries equal)
+  float lsum = 0.f;  // this lane's share (half of the keys) of its row's sum of the bf16 P
 
   LDS_AS char* kbuf = lds;
   LDS_AS char* vbuf = lds + C::NBUF * C::TILE_BYTES;
   const int ntiles = (it.kv_end + 63) >> 6;
   const int nfull = it.kv_end >> 6;                                  // tiles with every row < kv_end
   const int nplain = min(ntiles, mask_from / 64);  // tiles whose keys all lie below every row's limit
-  // prologue: K(0) V(0) K(1) V(1) K(2); S(0)
+  // prologue: K(0) V(0) K(1) V(1) K(2) and the page ids of the loads issued
+  // at t = 0 (tiles 2, 3, 4); S(0)
   PrefillLoop L;
   L.ntiles = ntiles;
   L.nfull = nfull;
-  L.slot = 0;
   for (int j = 0; j < 3 && j < ntiles; ++j) {
     prefill_issue_k<D>(p, it.hk, it.kv_end, j * 64, w, prefill_page<D>(p, ri, it.kv_end, j * 64, w), lane,
                        j < nfull, kbuf + j * C::TILE_BYTES);
@@ -689,30 +702,47 @@ __device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
       prefill_issue_v<D>(p, it.hk, it.kv_end, j * 64, w, prefill_page<D>(p, ri, it.kv_end, j * 64, w), lane,
                          j < nfull, vbuf + j * C::TILE_BYTES);
   }
-  L.pg_k = prefill_page<D>(p, ri, it.kv_end, 3 * 64, w);  // K(t + 3) at t = 0
-  L.pg_v = prefill_page<D>(p, ri, it.kv_end, 2 * 64, w);  // V(t + 2)
+#pragma unroll
+  for (int j = 0; j < 3; ++j) L.pg[j] = prefill_page<D>(p, ri, it.kv_end, (2 + j) * 64, w);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   const bool active = 32 * w < rows;  // waves whose rows are all padding skip the math
-  f32x16 s_cur[2];
-  if (active) prefill_scores<D>(kbuf, ln, qf, s_cur);
+  // Scores alternate between two register sets, sa holding S(kt) at the top
+  // of each unrolled pair, so no iteration copies them.
+  f32x16 sa[2], sb[2];
+  if (active) prefill_scores<D>(kbuf, ln, qf, sa);
   // iterations with a next tile (unmasked, then masked), then the last one
   const int last = ntiles - 1;
   const int n1 = min(nplain, last);
   int kt = 0;
-  for (; kt < n1; ++kt)
-    prefill_iter<D, false, true>(p, ri, it, kt, w, lane, active, lim, ln, qf, kbuf, vbuf, L, s_cur, m_ref,
-                                 lacc, oacc);
-  for (; kt < last; ++kt)
-    prefill_iter<D, true, true>(p, ri, it, kt, w, lane, active, lim, ln, qf, kbuf, vbuf, L, s_cur, m_ref,
-                                lacc, oacc);
+#define PD_PREFILL_ITER(MASK, NEXT, T, CUR, NXT)                                                            \
+  prefill_iter<D, MASK, NEXT>(p, ri, it, T, w, lane, active, lim, ln, qf, kbuf, vbuf, L, CUR, NXT, m_ref, lsum, \
+                              oacc)
+  for (; kt + 1 < n1; kt += 2) {
+    PD_PREFILL_ITER(false, true, kt, sa, sb);
+    PD_PREFILL_ITER(false, true, kt + 1, sb, sa);
+  }
+  if (kt < n1) {
+    PD_PREFILL_ITER(false, true, kt, sa, sb);
+    ++kt;
+    sa[0] = sb[0];
+    sa[1] = sb[1];
+  }
+  for (; kt + 1 < last; kt += 2) {
+    PD_PREFILL_ITER(true, true, kt, sa, sb);
+    PD_PREFILL_ITER(true, true, kt + 1, sb, sa);
+  }
+  if (kt < last) {
+    PD_PREFILL_ITER(true, true, kt, sa, sb);
+    sa[0] = sb[0];
+    sa[1] = sb[1];
+  }
   if (last < nplain)
-    prefill_iter<D, false, false>(p, ri, it, last, w, lane, active, lim, ln, qf, kbuf, vbuf, L, s_cur, m_ref,
-                                  lacc, oacc);
+    PD_PREFILL_ITER(false, false, last, sa, sb);
   else
-    prefill_iter<D, true, false>(p, ri, it, last, w, lane, active, lim, ln, qf, kbuf, vbuf, L, s_cur, m_ref,
-                                 lacc, oacc);
-  const float l_tot = lacc[0];
+    PD_PREFILL_ITER(true, false, last, sa, sb);
+#undef PD_PREFILL_ITER
+  const float l_tot = sum_x32(lsum);
   if (row_ok) {
     const float inv = 1.f / l_tot;
     float* op = p.out + qrow * D;
