@@ -517,6 +517,24 @@ __device__ __forceinline__ void prefill_scores(const LDS_AS char* kt, PrefillLan
 
 // Speculative softmax of one tile's scores (see kMaxTileSum above): returns
 // P in bf16 pairs, in the key order of the PV operand (pk[kb][4 sp + i]).
+// P = exp2(s c - mc) of one tile's scores, packed to bf16 in the key order of
+// the PV operand (pk[kb][4 sp + i]); returns this lane's sum of the rounded
+// P (v_dot2 against bf16 ones, two chains).
+template <int D>
+__device__ __forceinline__ float prefill_exp(const f32x16 (&s)[2], float cl, float mc, uint32_t (&pk)[2][8]) {
+  float t[2] = {0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pk[kb][i] = pack_bf16(fast_exp2(__builtin_fmaf(s[kb][2 * i], cl, -mc)),
+                            fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], cl, -mc)));
+      t[kb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[kb][i]),
+                                              __builtin_bit_cast(bf16x2, kBf16OnesPair), t[kb], false);
+    }
+  return t[0] + t[1];
+}
+
 template <int D, bool MASK>
 __device__ __forceinline__ void prefill_softmax(const AttnParams& p, f32x16 (&s)[2], int kbase, int lim,
                                                 PrefillLanes ln, float& m_ref, float& lsum,
@@ -530,16 +548,10 @@ __device__ __forceinline__ void prefill_softmax(const AttnParams& p, f32x16 (&s)
       for (int r = 0; r < 16; ++r)
         if (kbase + 32 * kb + 8 * (r >> 2) + 4 * ln.h2 + (r & 3) >= lim) s[kb][r] = -INFINITY;
   }
-  {
-    const float mc = m_ref * cl;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        pk[kb][i] = pack_bf16(fast_exp2(__builtin_fmaf(s[kb][2 * i], cl, -mc)),
-                              fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], cl, -mc)));
-  }
-  if (wave_any(p_out_of_range(pk[0]) | p_out_of_range(pk[1]))) {
+  float ts = prefill_exp<D>(s, cl, m_ref * cl, pk);
+  // Some P of the tile reached 2^64, or is inf / NaN (the first tile, with
+  // m_ref = -inf): this lane's sum of them shows it.
+  if (wave_any(!(ts < 0x1p64f))) {
     float mx = s[0][0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
@@ -552,14 +564,9 @@ __device__ __forceinline__ void prefill_softmax(const AttnParams& p, f32x16 (&s)
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) oacc[db] = oacc[db] * alpha;
     m_ref = m_new;
-    const float mc = m_ref * cl;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        pk[kb][i] = pack_bf16(fast_exp2(__builtin_fmaf(s[kb][2 * i], cl, -mc)),
-                              fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], cl, -mc)));
+    ts = prefill_exp<D>(s, cl, m_ref * cl, pk);
   }
+  lsum += ts;
 }
 
 // O^T += V^T P^T over the four 16-key k-steps of one tile.
@@ -632,12 +639,6 @@ __device__ __forceinline__ void prefill_iter(const AttnParams& p, const ReqInfo&
     if (NEXT) prefill_scores<D>(kbuf + ((t + 1) & 3) * C::TILE_BYTES, ln, qf, s_next);  // NEXT: t + 1 < ntiles
     uint32_t pk[2][8];
     prefill_softmax<D, MASK>(p, s_cur, t * 64, lim, ln, m_ref, lsum, oacc, pk);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[kb][i]),
-                                               __builtin_bit_cast(bf16x2, kBf16OnesPair), lsum, false);
     prefill_pv<D>(vbuf + (t & 3) * C::TILE_BYTES, ln, pk, oacc);
   }
 }
