@@ -106,10 +106,11 @@ typedef struct pd_attn_desc {
  *                      the planner choose; otherwise rounded up to 32
  *   num_cus            compute units to balance over; 0 = 256 (MI355X)
  *   block_order        order of the blocks of the attention launch:
- *                      0 = all prefill tiles, then all decode blocks
- *                          (default; the decode blocks fill the CUs freed by
- *                          the prefill tail); 1 = interleave prefill and
- *                          decode rounds by their cost at peak rates      */
+ *                      0 = interleave prefill and decode rounds by their
+ *                          cost at peak rates (default: CUs running decode
+ *                          blocks stream the cache while the others run
+ *                          prefill tiles); 1 = all prefill tiles, then all
+ *                          decode blocks                                   */
 typedef struct pd_plan_options {
   int32_t decode_chunk_keys;
   int32_t num_cus;

@@ -301,7 +301,7 @@ def test_block_map_covers_work_and_keeps_xcd_affinity(order):
             xcd_of_head.setdefault(int(pf[v][1]), set()).add(pos % 8)
     assert all(len(v) == 1 for v in xcd_of_head.values())
     assert len({next(iter(v)) for v in xcd_of_head.values()}) == 8
-    if order == 1:   # interleaved: decode blocks appear before the last prefill tile
+    if order == 0:   # interleaved (default): decode blocks appear before the last prefill tile
         first_d = int(np.argmax(bmap < 0))
         assert first_d < len(pf)
     else:            # prefill tiles first
