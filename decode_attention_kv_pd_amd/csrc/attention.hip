@@ -87,6 +87,14 @@ __device__ __forceinline__ void load_lds16(const void* src, LDS_AS char* lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
+// The same with the non-temporal hint, for the decode role's V stream (read
+// once).  Measured on MI355X over the long workload: decode-only 9 % faster,
+// the mixed launch 1 % faster.  (The same hint on the decode K loads into
+// registers made the mixed launch 8 % slower, so they keep the default.)
+__device__ __forceinline__ void load_lds16_nt(const void* src, LDS_AS char* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(m0) : "memory");
+}
 
 // Reductions across lane l and lane l ^ 32 / l ^ 16 (v_permlane*_swap).
 __device__ __forceinline__ float max_x32(float x) {
@@ -237,8 +245,8 @@ __device__ __forceinline__ void decode_issue(const AttnParams& p, const ReqInfo&
       for (int ks = 0; ks < C::KS; ++ks) kf[sb][ks] = *(const u32x4*)(kb + n * 2 * D + 16 * q + 64 * ks);
 #pragma unroll
       for (int i = 0; i < C::VLOADS / 2; ++i)
-        load_lds16(vb + (i * C::RPB + r) * 2 * D + 16 * c,
-                   stage + (sb * (C::VLOADS / 2) + i) * Lds<D>::BLOCK);
+        load_lds16_nt(vb + (i * C::RPB + r) * 2 * D + 16 * c,
+                      stage + (sb * (C::VLOADS / 2) + i) * Lds<D>::BLOCK);
     }
   } else {
 #pragma unroll
@@ -253,7 +261,7 @@ __device__ __forceinline__ void decode_issue(const AttnParams& p, const ReqInfo&
 #pragma unroll
       for (int i = 0; i < C::VLOADS / 2; ++i) {
         const int vrow = min(j0 + i * C::RPB + r, kvm1) & psm;
-        load_lds16(vb + vrow * 2 * D + 16 * c, stage + (sb * (C::VLOADS / 2) + i) * Lds<D>::BLOCK);
+        load_lds16_nt(vb + vrow * 2 * D + 16 * c, stage + (sb * (C::VLOADS / 2) + i) * Lds<D>::BLOCK);
       }
     }
   }
