@@ -74,6 +74,9 @@ __global__ __launch_bounds__(kBlockThreads) void append_kernel(AppendParams p) {
 // layer l is its K part then its V part, each seg_bytes long at seg_off in
 // its half (HND: a head range of a half is one contiguous run); in the
 // buffer it sits at ((l * n + i) * 2 + half) * seg_bytes.
+// Without a progress array the stores carry the non-temporal hint (each
+// byte is written once; measured on MI355X: pack 4.9 vs 4.6 TB/s, unpack 4.8
+// vs 4.2 TB/s, read + written).
 // With a progress array the copies are written through to memory (stores
 // coherent at system scope, so no L2 write-back is needed to publish them),
 // each block counts itself done once its stores are acknowledged, and the
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(kBlockThreads) void xfer_kernel(XferParams p) {
       const int64_t c = c0 + k * kBlockThreads;
       if (c < 2 * segc) {
         const int64_t pc = c < segc ? c * 16 : p.half_bytes + (c - segc) * 16;
-        *(u32x4*)(p.to_buffer ? buf + c * 16 : pg + pc) = v[k];
+        __builtin_nontemporal_store(v[k], (u32x4*)(p.to_buffer ? buf + c * 16 : pg + pc));
       }
     }
   } else {
