@@ -259,3 +259,138 @@ def device_seed(wid: int, rep: int, stream: int) -> int:
     sequence as the host draws (``stream`` separates Q / K-V / new tokens)."""
     ss = np.random.SeedSequence([SEED_ROOT, wid, rep, 1000 + stream])
     return int(ss.generate_state(1, np.uint64)[0] & np.uint64(0x7FFFFFFFFFFFFFFF))
+
+
+# ------------------------------------------------------------ MLA workloads
+# Latent KV cache (multi-head latent attention, post section "Sharded KV Cache
+# Transfers", DeepSeek paragraphs): one row of d_c + d_r values per token,
+# shared by every query head.  Dimensions are DeepSeek-V3's published
+# configuration (latent 512, rotary key 64, 128 query heads, softmax scale
+# 1 / sqrt(128 + 64)); the pages give none.
+#
+#   mla_tiny  3 requests, (qo, kv) = (1, 1), (2, 77), (1, 300); 16 heads,
+#             page size 16 (parity sizes)
+#   mla_tp8   64 decode requests, kv uniform in [1024, 8192]; 16 heads: one
+#             rank of an 8-way tensor-parallel decoder, which still holds the
+#             whole latent cache
+#   mla_dp    the same requests with all 128 heads: one rank of a
+#             data-parallel attention decoder
+MLA_WORKLOADS = {
+    6: dict(name="mla_tiny", H=16, ps=16),
+    7: dict(name="mla_tp8", H=16, ps=64),
+    8: dict(name="mla_dp", H=128, ps=64),
+}
+MLA_NAME_TO_ID = {v["name"]: k for k, v in MLA_WORKLOADS.items()}
+MLA_D_C = 512
+MLA_D_R = 64
+
+
+@dataclasses.dataclass
+class MlaBatch:
+    """One ragged MLA batch.  ``q`` [sum qo, H, d_c + d_r] and the logical
+    cache ``rows`` [sum kv, d_c + d_r] hold bf16 bit patterns (uint16)."""
+
+    wid: int
+    name: str
+    H: int
+    d_c: int
+    d_r: int
+    ps: int
+    causal: bool
+    sm_scale: float
+    qo_lens: np.ndarray
+    kv_lens: np.ndarray
+    page_indptr: np.ndarray
+    page_indices: np.ndarray
+    num_pool_pages: int
+    spare_pages: np.ndarray
+    q: Optional[np.ndarray] = None
+    rows: Optional[np.ndarray] = None
+    kv_indptr: Optional[np.ndarray] = None
+    qo_indptr: Optional[np.ndarray] = None
+
+    @property
+    def B(self) -> int:
+        return int(self.qo_lens.shape[0])
+
+    @property
+    def width(self) -> int:
+        return self.d_c + self.d_r
+
+    @property
+    def pool_shape(self):
+        return (self.num_pool_pages, self.ps, self.width)
+
+    @property
+    def page_bytes(self) -> int:
+        return self.ps * self.width * 2
+
+    def to_f64(self, a: np.ndarray) -> np.ndarray:
+        return bf16_bits_to_f32(a).astype(np.float64)
+
+    @property
+    def new_rows(self) -> np.ndarray:
+        """Rows [kv - qo, kv) of each request's cache, token-major."""
+        parts = []
+        for r in range(self.B):
+            s = int(self.kv_indptr[r])
+            kv, qo = int(self.kv_lens[r]), int(self.qo_lens[r])
+            parts.append(self.rows[s + kv - qo: s + kv])
+        return np.concatenate(parts, axis=0)
+
+    def request_pages(self, r: int) -> np.ndarray:
+        return self.page_indices[self.page_indptr[r]:self.page_indptr[r + 1]]
+
+
+def _mla_lengths(wid: int, rng: np.random.Generator):
+    if wid == 6:
+        return np.asarray([1, 2, 1], np.int32), np.asarray([1, 77, 300], np.int32)
+    if wid in (7, 8):
+        kv = rng.integers(1024, 8192, size=64, endpoint=True)
+        return np.ones(64, np.int32), kv.astype(np.int32)
+    raise ValueError(f"unknown MLA workload {wid}")
+
+
+def make_mla_batch(wid, rep: int = 0, materialize: bool = True, lengths=None, heads=None,
+                   page_size=None, causal=True, q_gain: float = 1.0,
+                   spare_frac: float = 0.05) -> MlaBatch:
+    """Build an MLA workload (id or name).  Random stream
+    ``SeedSequence([2026, wid, rep])`` drawn in the order lengths, pool
+    permutation, Q, cache rows; values N(0, 1) rounded to bf16 (nearest
+    even).  Spare pages and tail slots are left for the caller to poison."""
+    if isinstance(wid, str):
+        wid = MLA_NAME_TO_ID[wid]
+    spec = dict(MLA_WORKLOADS[wid])
+    if heads is not None:
+        spec["H"] = heads
+    if page_size is not None:
+        spec["ps"] = page_size
+    rng = np.random.default_rng(seed_sequence(wid, rep))
+    qo, kv = _mla_lengths(wid, rng)
+    if lengths is not None:
+        qo = np.asarray(lengths[0], np.int32)
+        kv = np.asarray(lengths[1], np.int32)
+    ps = spec["ps"]
+    npages = (kv.astype(np.int64) + ps - 1) // ps
+    total = int(npages.sum())
+    pool = max(total + 1, int(math.ceil(total * (1.0 + spare_frac))))
+    perm = rng.permutation(pool).astype(np.int32)
+    page_indptr = np.zeros(len(qo) + 1, np.int32)
+    page_indptr[1:] = np.cumsum(npages)
+    b = MlaBatch(wid=wid, name=spec["name"], H=spec["H"], d_c=MLA_D_C, d_r=MLA_D_R, ps=ps,
+                 causal=bool(causal), sm_scale=1.0 / math.sqrt(128 + MLA_D_R), qo_lens=qo, kv_lens=kv,
+                 page_indptr=page_indptr, page_indices=perm[:total].copy(), num_pool_pages=pool,
+                 spare_pages=perm[total:].copy())
+    b.qo_indptr = np.zeros(len(qo) + 1, np.int64)
+    b.qo_indptr[1:] = np.cumsum(qo)
+    b.kv_indptr = np.zeros(len(kv) + 1, np.int64)
+    b.kv_indptr[1:] = np.cumsum(kv)
+    if not materialize:
+        return b
+    nq, nk = int(b.qo_indptr[-1]), int(b.kv_indptr[-1])
+    q = rng.standard_normal((nq, b.H, b.width), dtype=np.float32)
+    if q_gain != 1.0:
+        q *= np.float32(q_gain)
+    rows = rng.standard_normal((nk, b.width), dtype=np.float32)
+    b.q, b.rows = f32_to_bf16_bits(q), f32_to_bf16_bits(rows)
+    return b
