@@ -20,6 +20,13 @@ The names mirror the C entry points of include/pd_attn.h:
   pd_xfer_upload(xfer, ws, stream=None)
   pd_kv_pack_layers(xfer, ws, buf, progress=None, stream=None)
   pd_kv_unpack_layers(xfer, ws, buf, progress=None, stream=None)
+  pd_mla_page_bytes(mdesc)                          -> int
+  pd_mla_plan(mdesc, qo_lens, kv_lens, page_indptr, page_indices, num_pool_pages,
+              decode_chunk_keys=0, num_cus=0)     -> Plan  (host only)
+  pd_mla_kv_append(plan, ws, kv_pool, rows_new, stream=None)
+  pd_mla_attention_run(plan, ws, q, kv_pool, out, lse=None, stream=None)
+  pd_mla_kv_pack(mdesc, kv_pool, num_pool_pages, page_ids, buf, scratch, stream=None)
+  pd_mla_kv_unpack(mdesc, kv_pool, num_pool_pages, page_ids, buf, scratch, stream=None)
 
 Device arguments are torch tensors (contiguous, on the GPU); host arrays are
 anything numpy can turn into int32.  Errors raise PdError carrying the
@@ -59,6 +66,13 @@ class pd_attn_desc(ctypes.Structure):
                 ("sm_scale", ctypes.c_float)]
 
 
+class pd_mla_desc(ctypes.Structure):
+    _fields_ = [("num_qo_heads", ctypes.c_int32), ("kv_lora_rank", ctypes.c_int32),
+                ("qk_rope_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float)]
+
+
 class pd_plan_options(ctypes.Structure):
     _fields_ = [("decode_chunk_keys", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("block_order", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
@@ -77,7 +91,8 @@ EXPORTS = ("pd_plan", "pd_plan_workspace_bytes", "pd_plan_upload", "pd_plan_get_
            "pd_kv_pack", "pd_kv_unpack", "pd_kv_pack_heads_bytes", "pd_kv_pack_heads", "pd_kv_unpack_heads",
            "pd_kv_shard_transfers", "pd_xfer_plan", "pd_xfer_buffer_bytes", "pd_xfer_workspace_bytes",
            "pd_xfer_upload", "pd_kv_pack_layers", "pd_kv_unpack_layers", "pd_xfer_free",
-           "pd_status_string", "pd_last_error", "pd_version")
+           "pd_mla_page_bytes", "pd_mla_plan", "pd_mla_kv_append", "pd_mla_attention_run", "pd_mla_kv_pack",
+           "pd_mla_kv_unpack", "pd_status_string", "pd_last_error", "pd_version")
 
 
 class pd_head_transfer(ctypes.Structure):
@@ -121,6 +136,13 @@ def _load():
         "pd_kv_pack_layers": (I32, [P, VP, VP, SZ, VP, VP]),
         "pd_kv_unpack_layers": (I32, [P, VP, VP, SZ, VP, VP]),
         "pd_xfer_free": (None, [P]),
+        "pd_mla_page_bytes": (SZ, [ctypes.POINTER(pd_mla_desc)]),
+        "pd_mla_plan": (I32, [ctypes.POINTER(pd_mla_desc), I32, pI32, pI32, pI32, pI32, I32,
+                              ctypes.POINTER(pd_plan_options), ctypes.POINTER(P)]),
+        "pd_mla_kv_append": (I32, [P, VP, VP, VP, VP]),
+        "pd_mla_attention_run": (I32, [P, VP, VP, VP, VP, VP, VP]),
+        "pd_mla_kv_pack": (I32, [ctypes.POINTER(pd_mla_desc), VP, I32, pI32, I32, VP, SZ, VP, SZ, VP]),
+        "pd_mla_kv_unpack": (I32, [ctypes.POINTER(pd_mla_desc), VP, I32, pI32, I32, VP, SZ, VP, SZ, VP]),
         "pd_status_string": (ctypes.c_char_p, [I32]),
         "pd_last_error": (ctypes.c_char_p, []),
         "pd_version": (ctypes.c_char_p, []),
@@ -395,3 +417,58 @@ def pd_kv_unpack_layers(xfer: XferPlan, ws, buf, progress=None, stream=None):
     _check(_lib.pd_kv_unpack_layers(xfer.handle, _dev(ws, "ws"), _dev(buf, "buf"),
                                     buf.numel() * buf.element_size(), _progress_ptr(progress),
                                     _stream(stream)))
+
+
+# ------------------------------------------------------------ latent (MLA) cache
+def make_mla_desc(num_qo_heads, page_size, causal=True, sm_scale=None, kv_lora_rank=512,
+                  qk_rope_dim=64) -> pd_mla_desc:
+    """sm_scale defaults to 1/sqrt(128 + qk_rope_dim) (DeepSeek-V3's query-key
+    head width)."""
+    if sm_scale is None:
+        sm_scale = 1.0 / float(128 + qk_rope_dim) ** 0.5
+    return pd_mla_desc(int(num_qo_heads), int(kv_lora_rank), int(qk_rope_dim), int(page_size), PD_BF16,
+                       int(bool(causal)), float(sm_scale))
+
+
+def pd_mla_page_bytes(mdesc) -> int:
+    return int(_lib.pd_mla_page_bytes(ctypes.byref(mdesc)))
+
+
+def pd_mla_plan(mdesc, qo_lens, kv_lens, page_indptr, page_indices, num_pool_pages,
+                decode_chunk_keys: int = 0, num_cus: int = 0) -> Plan:
+    qo, pqo = _i32(qo_lens)
+    kv, pkv = _i32(kv_lens)
+    ip, pip = _i32(page_indptr)
+    pi, ppi = _i32(page_indices)
+    if len(qo) != len(kv) or len(ip) != len(qo) + 1:
+        raise ValueError("qo_lens / kv_lens / page_indptr lengths disagree")
+    opts = pd_plan_options(int(decode_chunk_keys), int(num_cus), 0)
+    h = ctypes.c_void_p()
+    _check(_lib.pd_mla_plan(ctypes.byref(mdesc), len(qo), pqo, pkv, pip, ppi if len(pi) else None,
+                            int(num_pool_pages), ctypes.byref(opts), ctypes.byref(h)))
+    return Plan(h, mdesc)
+
+
+def pd_mla_kv_append(plan: Plan, ws, kv_pool, rows_new, stream=None):
+    _check(_lib.pd_mla_kv_append(plan.handle, _dev(ws, "ws"), _dev(kv_pool, "kv_pool"), _dev(rows_new, "rows_new"),
+                                 _stream(stream)))
+
+
+def pd_mla_attention_run(plan: Plan, ws, q, kv_pool, out, lse=None, stream=None):
+    _check(_lib.pd_mla_attention_run(plan.handle, _dev(ws, "ws"), _dev(q, "q"), _dev(kv_pool, "kv_pool"),
+                                     _dev(out, "out"), _dev(lse, "lse"), _stream(stream)))
+
+
+def pd_mla_kv_pack(mdesc, kv_pool, num_pool_pages, page_ids, buf, scratch, stream=None):
+    ids, pids = _i32(page_ids)
+    _check(_lib.pd_mla_kv_pack(ctypes.byref(mdesc), _dev(kv_pool, "kv_pool"), int(num_pool_pages), pids, len(ids),
+                               _dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(scratch, "scratch"),
+                               scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def pd_mla_kv_unpack(mdesc, kv_pool, num_pool_pages, page_ids, buf, scratch, stream=None):
+    ids, pids = _i32(page_ids)
+    _check(_lib.pd_mla_kv_unpack(ctypes.byref(mdesc), _dev(kv_pool, "kv_pool"), int(num_pool_pages), pids,
+                                 len(ids), _dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                 _dev(scratch, "scratch"), scratch.numel() * scratch.element_size(),
+                                 _stream(stream)))

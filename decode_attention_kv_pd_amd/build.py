@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpd_attn.so")
-SOURCES = [os.path.join(HERE, "csrc", n) for n in ("api.cpp", "attention.hip", "kv_ops.hip")]
+SOURCES = [os.path.join(HERE, "csrc", n) for n in ("api.cpp", "attention.hip", "mla.hip", "kv_ops.hip")]
 ARCH = "gfx950"
 
 

@@ -63,6 +63,25 @@ pd_status check_desc(const pd_attn_desc* d) {
 
 int elt_bytes(const pd_attn_desc* d) { return d->dtype == PD_F32 ? 4 : 2; }
 
+pd_status check_mla_desc(const pd_mla_desc* d) {
+  if (!d) return fail(PD_ERR_INVALID_ARG, "desc is NULL");
+  if (d->kv_lora_rank != pdk::kMlaLatent || d->qk_rope_dim != pdk::kMlaRope)
+    return fail(PD_ERR_UNSUPPORTED, "kv_lora_rank must be 512 and qk_rope_dim 64");
+  if (d->num_qo_heads < 16 || d->num_qo_heads > 128 || d->num_qo_heads % 16 != 0)
+    return fail(PD_ERR_UNSUPPORTED, "num_qo_heads must be a multiple of 16 in [16, 128]");
+  if (d->page_size != 16 && d->page_size != 32 && d->page_size != 64 && d->page_size != 128)
+    return fail(PD_ERR_UNSUPPORTED, "page_size must be 16, 32, 64 or 128");
+  if (d->dtype != PD_BF16) return fail(PD_ERR_UNSUPPORTED, "dtype must be PD_BF16");
+  if (d->causal != 0 && d->causal != 1) return fail(PD_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!std::isfinite(d->sm_scale) || !(d->sm_scale > 0.f))
+    return fail(PD_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  return PD_OK;
+}
+
+int64_t mla_page_bytes_of(const pd_mla_desc* d) {
+  return (int64_t)d->page_size * (d->kv_lora_rank + d->qk_rope_dim) * 2;
+}
+
 int64_t page_bytes_of(const pd_attn_desc* d) {
   return 2LL * d->num_kv_heads * d->page_size * d->head_dim * elt_bytes(d);
 }
@@ -83,6 +102,12 @@ struct pd_plan_s {
   size_t meta_bytes = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   int64_t prefill_flops = 0, decode_bytes = 0;
   std::vector<char> blob;  // host image of the workspace tables
+  // latent-cache (MLA) plans: pd_mla_plan fills these instead of pf / du / mg
+  bool mla = false;
+  pd_mla_desc mdesc{};
+  std::vector<pdk::MlaItem> mitems;  // launch order
+  std::vector<pdk::MlaMergeGroup> mmg;
+  size_t off_mitems = 0, off_mmg = 0;
 };
 
 // A multi-layer transfer: the listed pages' heads [h0, h1) of L layer pools.
@@ -338,6 +363,50 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   return PD_OK;
 }
 
+// Checks a batch's lengths and page table (page size ps) and fills the
+// plan's request rows and page list.
+pd_status fill_requests(pd_plan_s& P, int ps, int32_t batch, const int32_t* qo_lens, const int32_t* kv_lens,
+                        const int32_t* page_indptr, const int32_t* page_indices, int32_t num_pool_pages) {
+  if (page_indptr[0] != 0) return fail(PD_ERR_INVALID_ARG, "page_indptr[0] must be 0");
+  int64_t rows = 0;
+  for (int r = 0; r < batch; ++r) {
+    const int32_t qo = qo_lens[r], kv = kv_lens[r];
+    if (qo < 0 || kv < 0) return fail(PD_ERR_INVALID_ARG, "request " + std::to_string(r) + ": negative length");
+    if (qo > kv)
+      return fail(PD_ERR_INVALID_ARG, "request " + std::to_string(r) + ": qo_len > kv_len (the new tokens are part of the cache)");
+    const int64_t need = ((int64_t)kv + ps - 1) / ps;
+    const int64_t have = (int64_t)page_indptr[r + 1] - page_indptr[r];
+    if (have != need)
+      return fail(PD_ERR_INVALID_ARG, "request " + std::to_string(r) + ": has " + std::to_string(have) +
+                                          " pages, needs ceil(kv_len / page_size) = " + std::to_string(need));
+    rows += qo;
+  }
+  if (rows > INT32_MAX) return fail(PD_ERR_INVALID_ARG, "too many query rows");
+  const int64_t total_pages = page_indptr[batch];
+  if (total_pages > 0 && !page_indices) return fail(PD_ERR_INVALID_ARG, "page_indices is NULL");
+  {
+    std::vector<uint8_t> seen((size_t)std::max(num_pool_pages, 1), 0);
+    for (int64_t i = 0; i < total_pages; ++i) {
+      const int32_t id = page_indices[i];
+      if (id < 0 || id >= num_pool_pages)
+        return fail(PD_ERR_OUT_OF_RANGE, "page id " + std::to_string(id) + " outside the pool");
+      if (seen[id]) return fail(PD_ERR_INVALID_ARG, "page id " + std::to_string(id) + " appears twice");
+      seen[id] = 1;
+    }
+  }
+  P.B = batch;
+  P.total_rows = (int32_t)rows;
+  P.qo_indptr.resize(batch + 1);
+  P.req.resize(batch);
+  P.qo_indptr[0] = 0;
+  for (int r = 0; r < batch; ++r) {
+    P.req[r] = {P.qo_indptr[r], qo_lens[r], kv_lens[r], page_indptr[r]};
+    P.qo_indptr[r + 1] = P.qo_indptr[r] + qo_lens[r];
+  }
+  P.pages.assign(page_indices, page_indices + total_pages);
+  return PD_OK;
+}
+
 pdk::AttnParams attn_params(const pd_plan_s& P, void* d_ws) {
   char* ws = (char*)d_ws;
   pdk::AttnParams a{};
@@ -365,6 +434,132 @@ pdk::AttnParams attn_params(const pd_plan_s& P, void* d_ws) {
   a.sm_scale = P.desc.sm_scale;
   a.c_log2 = P.desc.sm_scale * 1.4426950408889634f;
   a.page_elems = 2LL * P.desc.num_kv_heads * P.desc.page_size * P.desc.head_dim;
+  return a;
+}
+
+// Latent-cache plan: blocks of 64 query rows of one request over a chunk of
+// keys.  Each (request, row group) is cut into chunks of equal length (a
+// multiple of 32 keys) so that about two blocks per CU exist; the blocks of
+// one (request, chunk) read the same cache rows and are placed on one XCD,
+// one dispatch round apart (block i runs on XCD i % 8), longest first.
+pd_status build_mla_plan(pd_plan_s& P, const pd_plan_options* opts) {
+  const pd_mla_desc& d = P.mdesc;
+  const int H = d.num_qo_heads;
+  const int num_cus = (opts && opts->num_cus > 0) ? opts->num_cus : 256;
+  int64_t work = 0;  // row groups x keys
+  for (int r = 0; r < P.B; ++r) {
+    const pdk::ReqInfo& ri = P.req[r];
+    if (ri.qo == 0) continue;
+    const int ng = (int)(((int64_t)ri.qo * H + pdk::kMlaRows - 1) / pdk::kMlaRows);
+    work += (int64_t)ng * ri.kv;
+    P.decode_bytes += (int64_t)ri.kv * pdk::kMlaWidth * 2;
+  }
+  int chunk = 0;
+  if (opts && opts->decode_chunk_keys > 0) {
+    chunk = (opts->decode_chunk_keys + 31) / 32 * 32;
+  } else if (work > 0) {
+    int64_t c = (work + 2LL * num_cus - 1) / (2LL * num_cus);
+    c = (c + 127) / 128 * 128;
+    chunk = (int)std::min<int64_t>(std::max<int64_t>(c, 256), 16384);
+  }
+  P.chunk_keys = chunk;
+  struct Task {  // one (request, chunk): its row groups' blocks
+    int req, c, k0, k1, ng;
+  };
+  std::vector<Task> tasks;
+  std::vector<int> base(P.B, -1), nchunks(P.B, 1);  // first partial slot of a split request, chunks
+  for (int r = 0; r < P.B; ++r) {
+    const pdk::ReqInfo& ri = P.req[r];
+    if (ri.qo == 0) continue;
+    const int ng = (int)(((int64_t)ri.qo * H + pdk::kMlaRows - 1) / pdk::kMlaRows);
+    int nch = (ri.kv + chunk - 1) / chunk;
+    int len = (ri.kv + nch - 1) / nch;
+    len = (len + 31) / 32 * 32;
+    nch = (ri.kv + len - 1) / len;
+    nchunks[r] = nch;
+    if (nch > 1) {  // slots [base, base + ng * nch): row group rg's chunk c at base + rg * nch + c
+      base[r] = P.n_parts;
+      for (int rg = 0; rg < ng; ++rg) P.mmg.push_back({r, rg, P.n_parts + rg * nch, nch});
+      P.n_parts += ng * nch;
+    }
+    for (int c = 0; c < nch; ++c) tasks.push_back({r, c, c * len, std::min(ri.kv, (c + 1) * len), ng});
+  }
+  std::stable_sort(tasks.begin(), tasks.end(),
+                   [](const Task& a, const Task& b) { return (a.k1 - a.k0) > (b.k1 - b.k0); });
+  std::vector<std::vector<pdk::MlaItem>> xq(kNumXcd);
+  std::vector<int64_t> xload(kNumXcd, 0);
+  for (const Task& t : tasks) {
+    const int x = (int)(std::min_element(xload.begin(), xload.end()) - xload.begin());
+    xload[x] += (int64_t)t.ng * (t.k1 - t.k0);
+    for (int rg = 0; rg < t.ng; ++rg)
+      xq[x].push_back({t.req, rg, t.k0, t.k1, base[t.req] < 0 ? -1 : base[t.req] + rg * nchunks[t.req] + t.c,
+                       0, 0, 0});
+  }
+  size_t total = 0;
+  for (auto& q : xq) total += q.size();
+  std::vector<size_t> head(kNumXcd, 0);
+  P.mitems.reserve(total);
+  for (size_t i = 0; i < total; ++i) {
+    int x = (int)(i % kNumXcd);
+    if (head[x] >= xq[x].size()) {  // this XCD ran out: take from the fullest
+      size_t best = 0;
+      int bx = -1;
+      for (int y = 0; y < kNumXcd; ++y)
+        if (xq[y].size() - head[y] > best) best = xq[y].size() - head[y], bx = y;
+      x = bx;
+    }
+    P.mitems.push_back(xq[x][head[x]++]);
+  }
+
+  size_t off = 0;
+  P.off_qo = off;
+  off = align_up(off + sizeof(int32_t) * (P.B + 1));
+  P.off_req = off;
+  off = align_up(off + sizeof(pdk::ReqInfo) * P.B);
+  P.off_pages = off;
+  off = align_up(off + sizeof(int32_t) * P.pages.size());
+  P.off_mitems = off;
+  off = align_up(off + sizeof(pdk::MlaItem) * P.mitems.size());
+  P.off_mmg = off;
+  off = align_up(off + sizeof(pdk::MlaMergeGroup) * P.mmg.size());
+  P.meta_bytes = off;
+  P.off_part_o = off;
+  off = align_up(off + sizeof(float) * (size_t)P.n_parts * pdk::kMlaRows * pdk::kMlaLatent);
+  P.off_part_lse = off;
+  off = align_up(off + sizeof(float) * (size_t)P.n_parts * pdk::kMlaRows);
+  P.ws_bytes = off;
+  P.blob.assign(P.meta_bytes, 0);
+  auto put = [&](size_t o, const void* src, size_t n) {
+    if (n) std::memcpy(P.blob.data() + o, src, n);
+  };
+  put(P.off_qo, P.qo_indptr.data(), sizeof(int32_t) * P.qo_indptr.size());
+  put(P.off_req, P.req.data(), sizeof(pdk::ReqInfo) * P.req.size());
+  put(P.off_pages, P.pages.data(), sizeof(int32_t) * P.pages.size());
+  put(P.off_mitems, P.mitems.data(), sizeof(pdk::MlaItem) * P.mitems.size());
+  put(P.off_mmg, P.mmg.data(), sizeof(pdk::MlaMergeGroup) * P.mmg.size());
+  return PD_OK;
+}
+
+pdk::MlaParams mla_params(const pd_plan_s& P, void* d_ws) {
+  char* ws = (char*)d_ws;
+  pdk::MlaParams a{};
+  a.qo_indptr = (const int32_t*)(ws + P.off_qo);
+  a.req = (const pdk::ReqInfo*)(ws + P.off_req);
+  a.page_indices = (const int32_t*)(ws + P.off_pages);
+  a.items = (const pdk::MlaItem*)(ws + P.off_mitems);
+  a.mg = (const pdk::MlaMergeGroup*)(ws + P.off_mmg);
+  a.part_o = (float*)(ws + P.off_part_o);
+  a.part_lse = (float*)(ws + P.off_part_lse);
+  a.n_items = (int32_t)P.mitems.size();
+  a.n_mg = (int32_t)P.mmg.size();
+  a.B = P.B;
+  a.total_rows = P.total_rows;
+  a.H = P.mdesc.num_qo_heads;
+  a.ps = P.mdesc.page_size;
+  a.ps_shift = __builtin_ctz((unsigned)P.mdesc.page_size);
+  a.causal = P.mdesc.causal;
+  a.sm_scale = P.mdesc.sm_scale;
+  a.c_log2 = P.mdesc.sm_scale * 1.4426950408889634f;
   return a;
 }
 
@@ -504,47 +699,14 @@ pd_status pd_plan(const pd_attn_desc* desc, int32_t batch, const int32_t* qo_len
       return fail(PD_ERR_INVALID_ARG, "negative planner option");
     if (opts && opts->block_order != 0 && opts->block_order != 1)
       return fail(PD_ERR_INVALID_ARG, "block_order must be 0 or 1");
-    const int ps = desc->page_size;
-    if (page_indptr[0] != 0) return fail(PD_ERR_INVALID_ARG, "page_indptr[0] must be 0");
-    int64_t rows = 0;
-    for (int r = 0; r < batch; ++r) {
-      const int32_t qo = qo_lens[r], kv = kv_lens[r];
-      if (qo < 0 || kv < 0) return fail(PD_ERR_INVALID_ARG, "request " + std::to_string(r) + ": negative length");
-      if (qo > kv)
-        return fail(PD_ERR_INVALID_ARG, "request " + std::to_string(r) + ": qo_len > kv_len (the new tokens are part of the cache)");
-      const int64_t need = ((int64_t)kv + ps - 1) / ps;
-      const int64_t have = (int64_t)page_indptr[r + 1] - page_indptr[r];
-      if (have != need)
-        return fail(PD_ERR_INVALID_ARG, "request " + std::to_string(r) + ": has " + std::to_string(have) +
-                                            " pages, needs ceil(kv_len / page_size) = " + std::to_string(need));
-      rows += qo;
-    }
-    if (rows > INT32_MAX) return fail(PD_ERR_INVALID_ARG, "too many query rows");
-    const int64_t total_pages = page_indptr[batch];
-    if (total_pages > 0 && !page_indices) return fail(PD_ERR_INVALID_ARG, "page_indices is NULL");
-    {
-      std::vector<uint8_t> seen((size_t)std::max(num_pool_pages, 1), 0);
-      for (int64_t i = 0; i < total_pages; ++i) {
-        const int32_t id = page_indices[i];
-        if (id < 0 || id >= num_pool_pages)
-          return fail(PD_ERR_OUT_OF_RANGE, "page id " + std::to_string(id) + " outside the pool");
-        if (seen[id]) return fail(PD_ERR_INVALID_ARG, "page id " + std::to_string(id) + " appears twice");
-        seen[id] = 1;
-      }
-    }
     pd_plan_s* P = new pd_plan_s();
-    P->desc = *desc;
-    P->B = batch;
-    P->g = desc->num_qo_heads / desc->num_kv_heads;
-    P->total_rows = (int32_t)rows;
-    P->qo_indptr.resize(batch + 1);
-    P->req.resize(batch);
-    P->qo_indptr[0] = 0;
-    for (int r = 0; r < batch; ++r) {
-      P->req[r] = {P->qo_indptr[r], qo_lens[r], kv_lens[r], page_indptr[r]};
-      P->qo_indptr[r + 1] = P->qo_indptr[r] + qo_lens[r];
+    s = fill_requests(*P, desc->page_size, batch, qo_lens, kv_lens, page_indptr, page_indices, num_pool_pages);
+    if (s != PD_OK) {
+      delete P;
+      return s;
     }
-    P->pages.assign(page_indices, page_indices + total_pages);
+    P->desc = *desc;
+    P->g = desc->num_qo_heads / desc->num_kv_heads;
     s = build_plan(*P, opts);
     if (s != PD_OK) {
       delete P;
@@ -566,8 +728,15 @@ pd_status pd_plan_get_stats(pd_plan_t plan, pd_plan_stats* out) {
   out->batch = plan->B;
   out->total_q_rows = plan->total_rows;
   out->prefill_tiles = (int32_t)plan->pf.size();
-  out->decode_units = (int32_t)plan->du.size();
-  out->decode_row_groups = (int32_t)plan->mg.size();
+  out->decode_units = (int32_t)(plan->mla ? plan->mitems.size() : plan->du.size());
+  if (plan->mla) {
+    int32_t groups = 0;
+    for (const auto& ri : plan->req)
+      groups += (int32_t)(((int64_t)ri.qo * plan->mdesc.num_qo_heads + pdk::kMlaRows - 1) / pdk::kMlaRows);
+    out->decode_row_groups = groups;
+  } else {
+    out->decode_row_groups = (int32_t)plan->mg.size();
+  }
   out->decode_chunk_keys = plan->chunk_keys;
   out->prefill_flops = plan->prefill_flops;
   out->decode_kv_bytes = plan->decode_bytes;
@@ -581,8 +750,22 @@ int32_t pd_plan_work_items(pd_plan_t plan, int32_t kind, int32_t* out, int32_t m
   size_t count, width;
   switch (kind) {
     case 0: src = (const int32_t*)plan->pf.data(); count = plan->pf.size(); width = 8; break;
-    case 1: src = (const int32_t*)plan->du.data(); count = plan->du.size(); width = 8; break;
-    case 2: src = (const int32_t*)plan->mg.data(); count = plan->mg.size(); width = 4; break;
+    case 1:
+      if (plan->mla) {
+        src = (const int32_t*)plan->mitems.data(); count = plan->mitems.size();
+      } else {
+        src = (const int32_t*)plan->du.data(); count = plan->du.size();
+      }
+      width = 8;
+      break;
+    case 2:
+      if (plan->mla) {
+        src = (const int32_t*)plan->mmg.data(); count = plan->mmg.size();
+      } else {
+        src = (const int32_t*)plan->mg.data(); count = plan->mg.size();
+      }
+      width = 4;
+      break;
     case 3: src = plan->block_map.data(); count = plan->block_map.size(); width = 1; break;
     default: return fail(PD_ERR_INVALID_ARG, "unknown work item kind");
   }
@@ -610,6 +793,7 @@ void pd_plan_free(pd_plan_t plan) { delete plan; }
 pd_status pd_kv_append(pd_plan_t plan, void* d_ws, void* kv_pool, const void* k_new, const void* v_new,
                        void* stream) {
   if (!plan || !d_ws) return fail(PD_ERR_INVALID_ARG, "NULL plan or workspace");
+  if (plan->mla) return fail(PD_ERR_INVALID_ARG, "an MLA plan: use pd_mla_kv_append");
   if (plan->total_rows == 0) return PD_OK;
   if (!kv_pool || !k_new || !v_new) return fail(PD_ERR_INVALID_ARG, "NULL pool or K/V pointer");
   char* ws = (char*)d_ws;
@@ -634,6 +818,7 @@ pd_status pd_kv_append(pd_plan_t plan, void* d_ws, void* kv_pool, const void* k_
 pd_status pd_attention_run(pd_plan_t plan, void* d_ws, const void* q, const void* kv_pool, float* out,
                            float* lse, void* stream) {
   if (!plan || !d_ws) return fail(PD_ERR_INVALID_ARG, "NULL plan or workspace");
+  if (plan->mla) return fail(PD_ERR_INVALID_ARG, "an MLA plan: use pd_mla_attention_run");
   if (plan->total_rows == 0) return PD_OK;
   if (!q || !kv_pool || !out) return fail(PD_ERR_INVALID_ARG, "NULL q, pool or out");
   pdk::AttnParams a = attn_params(*plan, d_ws);
@@ -804,6 +989,125 @@ pd_status pd_kv_unpack_layers(pd_xfer_t x, void* d_ws, const void* d_buf, size_t
 }
 
 void pd_xfer_free(pd_xfer_t x) { delete x; }
+
+size_t pd_mla_page_bytes(const pd_mla_desc* desc) {
+  if (!desc || desc->page_size < 1 || desc->kv_lora_rank < 1 || desc->qk_rope_dim < 0) return 0;
+  return (size_t)mla_page_bytes_of(desc);
+}
+
+pd_status pd_mla_plan(const pd_mla_desc* desc, int32_t batch, const int32_t* qo_lens, const int32_t* kv_lens,
+                      const int32_t* page_indptr, const int32_t* page_indices, int32_t num_pool_pages,
+                      const pd_plan_options* opts, pd_plan_t* out) {
+  try {
+    if (!out) return fail(PD_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    pd_status s = check_mla_desc(desc);
+    if (s != PD_OK) return s;
+    if (batch < 1) return fail(PD_ERR_INVALID_ARG, "batch must be >= 1");
+    if (!qo_lens || !kv_lens || !page_indptr) return fail(PD_ERR_INVALID_ARG, "NULL length or indptr array");
+    if (num_pool_pages < 0) return fail(PD_ERR_INVALID_ARG, "num_pool_pages must be >= 0");
+    if (opts && (opts->decode_chunk_keys < 0 || opts->num_cus < 0))
+      return fail(PD_ERR_INVALID_ARG, "negative planner option");
+    pd_plan_s* P = new pd_plan_s();
+    s = fill_requests(*P, desc->page_size, batch, qo_lens, kv_lens, page_indptr, page_indices, num_pool_pages);
+    if (s == PD_OK) {
+      P->mla = true;
+      P->mdesc = *desc;
+      s = build_mla_plan(*P, opts);
+    }
+    if (s != PD_OK) {
+      delete P;
+      return s;
+    }
+    *out = P;
+    return PD_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(PD_ERR_NO_MEMORY, "host allocation failed");
+  } catch (...) {
+    return fail(PD_ERR_INVALID_ARG, "unexpected error while planning");
+  }
+}
+
+pd_status pd_mla_kv_append(pd_plan_t plan, void* d_ws, void* kv_pool, const void* rows_new, void* stream) {
+  if (!plan || !d_ws) return fail(PD_ERR_INVALID_ARG, "NULL plan or workspace");
+  if (!plan->mla) return fail(PD_ERR_INVALID_ARG, "not an MLA plan: use pd_kv_append");
+  if (plan->total_rows == 0) return PD_OK;
+  if (!kv_pool || !rows_new) return fail(PD_ERR_INVALID_ARG, "NULL pool or rows pointer");
+  pdk::MlaParams a = mla_params(*plan, d_ws);
+  hipError_t e = pdk::launch_mla_append(a, kv_pool, rows_new, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "MLA append launch");
+  return PD_OK;
+}
+
+pd_status pd_mla_attention_run(pd_plan_t plan, void* d_ws, const void* q, const void* kv_pool, float* out,
+                               float* lse, void* stream) {
+  if (!plan || !d_ws) return fail(PD_ERR_INVALID_ARG, "NULL plan or workspace");
+  if (!plan->mla) return fail(PD_ERR_INVALID_ARG, "not an MLA plan: use pd_attention_run");
+  if (plan->total_rows == 0) return PD_OK;
+  if (!q || !kv_pool || !out) return fail(PD_ERR_INVALID_ARG, "NULL q, pool or out");
+  pdk::MlaParams a = mla_params(*plan, d_ws);
+  a.q = q;
+  a.pool = kv_pool;
+  a.out = out;
+  a.lse = lse;
+  hipError_t e = pdk::launch_mla(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "MLA attention launch");
+  return PD_OK;
+}
+
+namespace {
+pd_status mla_xfer(const pd_mla_desc* desc, const void* pool, const void* buf, int32_t num_pool_pages,
+                   const int32_t* ids, int32_t n, size_t buf_bytes, void* scratch, size_t scratch_bytes,
+                   void* stream, bool to_buffer) {
+  pd_status s = check_mla_desc(desc);
+  if (s != PD_OK) return s;
+  if (n < 0) return fail(PD_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return PD_OK;
+  if (!ids || !pool || !buf || !scratch) return fail(PD_ERR_INVALID_ARG, "NULL pointer argument");
+  const int64_t pb = mla_page_bytes_of(desc);
+  if (buf_bytes < (size_t)n * (size_t)pb) return fail(PD_ERR_WORKSPACE, "buffer smaller than the n pages");
+  if (scratch_bytes < sizeof(int32_t) * (size_t)n) return fail(PD_ERR_WORKSPACE, "scratch smaller than 4 * n bytes");
+  if ((s = check_ids(num_pool_pages, ids, n)) != PD_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if ((s = staged_upload(scratch, ids, sizeof(int32_t) * (size_t)n, st)) != PD_OK) return s;
+  pdk::XferParams p{};
+  p.buf = (char*)buf;
+  p.pool0 = (void*)pool;
+  p.page_ids = (const int32_t*)scratch;
+  p.page_bytes = pb;
+  p.half_bytes = pb / 2;  // a page moves as two halves of one contiguous image
+  p.seg_off = 0;
+  p.seg_bytes = pb / 2;
+  p.n = n;
+  p.L = 1;
+  p.to_buffer = to_buffer ? 1 : 0;
+  hipError_t e = pdk::launch_xfer(p, st);
+  if (e != hipSuccess) return hip_fail(e, to_buffer ? "MLA pack launch" : "MLA unpack launch");
+  return PD_OK;
+}
+}  // namespace
+
+pd_status pd_mla_kv_pack(const pd_mla_desc* desc, const void* kv_pool, int32_t num_pool_pages,
+                         const int32_t* page_ids, int32_t n, void* d_buf, size_t buf_bytes, void* d_scratch,
+                         size_t scratch_bytes, void* stream) {
+  try {
+    return mla_xfer(desc, kv_pool, d_buf, num_pool_pages, page_ids, n, buf_bytes, d_scratch, scratch_bytes, stream,
+                    true);
+  } catch (...) {
+    return fail(PD_ERR_NO_MEMORY, "host allocation failed");
+  }
+}
+
+pd_status pd_mla_kv_unpack(const pd_mla_desc* desc, void* kv_pool, int32_t num_pool_pages,
+                           const int32_t* page_ids, int32_t n, const void* d_buf, size_t buf_bytes,
+                           void* d_scratch, size_t scratch_bytes, void* stream) {
+  try {
+    return mla_xfer(desc, kv_pool, d_buf, num_pool_pages, page_ids, n, buf_bytes, d_scratch, scratch_bytes, stream,
+                    false);
+  } catch (...) {
+    return fail(PD_ERR_NO_MEMORY, "host allocation failed");
+  }
+}
 
 const char* pd_status_string(pd_status s) {
   switch (s) {

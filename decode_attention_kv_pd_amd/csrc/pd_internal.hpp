@@ -96,6 +96,48 @@ struct XferParams {
   int32_t to_buffer;         // 1: pool -> buffer (pack), 0: buffer -> pool (unpack)
 };
 
+// ---- MLA decode over a latent cache (pool [pages][ps][kMlaWidth] bf16: per
+// token the kMlaLatent latent entries, then the kMlaRope rotary-key entries).
+constexpr int kMlaLatent = 512;
+constexpr int kMlaRope = 64;
+constexpr int kMlaWidth = kMlaLatent + kMlaRope;
+constexpr int kMlaWaves = 4;                   // wavefronts per block
+constexpr int kMlaThreads = 64 * kMlaWaves;
+constexpr int kMlaRows = 16 * kMlaWaves;       // query rows per block (16 per wavefront)
+
+// One block of the MLA kernel: query rows [64 rg, 64 rg + 64) of request
+// `req` (row n = token n / H, head n % H) over keys [k0, k1).  part >= 0:
+// the partial result goes to slot `part`; part < 0: straight to out / lse.
+struct MlaItem {
+  int32_t req, rg, k0, k1, part, rsv0, rsv1, rsv2;
+};
+
+// Partial results [part0, part0 + nparts) of one (request, row group).
+struct MlaMergeGroup {
+  int32_t req, rg, part0, nparts;
+};
+
+struct MlaParams {
+  const void* q;      // [rows][H][kMlaWidth] bf16
+  const void* pool;   // [pages][ps][kMlaWidth] bf16
+  float* out;         // [rows][H][kMlaLatent]
+  float* lse;         // [rows][H], may be null
+  const int32_t* qo_indptr;
+  const ReqInfo* req;
+  const int32_t* page_indices;
+  const MlaItem* items;
+  const MlaMergeGroup* mg;
+  float* part_o;      // [n_parts][kMlaRows][kMlaLatent]
+  float* part_lse;    // [n_parts][kMlaRows]
+  int32_t n_items, n_mg, B, total_rows;
+  int32_t H, ps, ps_shift, causal;
+  float sm_scale;
+  float c_log2;       // sm_scale * log2(e)
+};
+
+hipError_t launch_mla(const MlaParams& p, hipStream_t s);
+hipError_t launch_mla_append(const MlaParams& p, void* pool, const void* rows_new, hipStream_t s);
+
 hipError_t launch_attention(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_merge(const AttnParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);

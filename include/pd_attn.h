@@ -16,6 +16,10 @@
  *   pd_xfer_plan, pd_kv_pack_layers, pd_kv_unpack_layers
  *                    several layers' pages in one launch, with a per-layer
  *                    completion counter a host thread can poll
+ *   pd_mla_plan, pd_mla_kv_append, pd_mla_attention_run, pd_mla_kv_pack,
+ *   pd_mla_kv_unpack
+ *                    the same steps for a latent (MLA) KV cache: one row
+ *                    per token shared by every query head
  *
  * What the operations compute follows the Perplexity post "Disaggregated
  * prefill and decode" and the kwkr.cn PD-disaggregation survey; each entry
@@ -391,6 +395,99 @@ pd_status pd_kv_unpack_layers(pd_xfer_t xfer, void* d_ws, const void* d_buf,
 
 /* Release a transfer plan (host memory only). */
 void pd_xfer_free(pd_xfer_t xfer);
+
+/* ---- MLA decode over a latent KV cache --------------------------------
+ * Perplexity, "Disaggregated prefill and decode", section "Sharded KV Cache
+ * Transfers" (DeepSeek paragraphs): multi-head latent attention compresses
+ * every KV head of a token into one latent vector, so tensor parallelism
+ * cannot split the cache by heads.  Every rank holds the same latent cache,
+ * and the heads are only separated after decompression.  The pages give no
+ * formula.  These calls compute the absorbed decode form, the plainest reading:
+ *   cache row of token j:  row_j = [ latent_j (kv_lora_rank) ;
+ *                                    rotary key_j (qk_rope_dim) ]
+ *   query row (token t, head h): q = [ absorbed latent query ; rotary query ]
+ *   S_j = sm_scale * <q, row_j>   over the visible keys (end-aligned causal
+ *                                 mask as above, or all keys)
+ *   O[t,h]   = sum_j softmax_j(S) latent_j          (kv_lora_rank floats)
+ *   LSE[t,h] = ln sum_j exp(S_j)
+ * i.e. one-KV-head attention whose key is the whole row and whose value is
+ * its latent part.  The up-projection of the values (and of the queries'
+ * latent part) stays outside this step.
+ *
+ * Layouts (row-major):
+ *   latent pool [num_pool_pages][page_size][kv_lora_rank + qk_rope_dim] bf16;
+ *               token t of request r in page page_indices[page_indptr[r] +
+ *               t / page_size], slot t % page_size; a page is one
+ *               contiguous image, identical on every rank
+ *   q           [sum qo][num_qo_heads][kv_lora_rank + qk_rope_dim] bf16
+ *   rows_new    [sum qo][kv_lora_rank + qk_rope_dim] bf16
+ *   out         [sum qo][num_qo_heads][kv_lora_rank] float32
+ *   lse         [sum qo][num_qo_heads] float32
+ * Ownership, streams and errors as for the calls above. */
+typedef struct pd_mla_desc {
+  int32_t num_qo_heads;  /* query heads on this rank: 16, 32, ..., 128 */
+  int32_t kv_lora_rank;  /* latent entries per token: 512 */
+  int32_t qk_rope_dim;   /* rotary-key entries per token: 64 */
+  int32_t page_size;     /* tokens per page: 16, 32, 64 or 128 */
+  int32_t dtype;         /* PD_BF16 */
+  int32_t causal;        /* 1: end-aligned causal mask; 0: all kv keys */
+  float sm_scale;        /* > 0 (DeepSeek: 1/sqrt(qk_nope + qk_rope dims)) */
+} pd_mla_desc;
+
+/* Bytes of one latent page: page_size * (kv_lora_rank + qk_rope_dim) * 2;
+ * 0 for an invalid desc. */
+size_t pd_mla_page_bytes(const pd_mla_desc* desc);
+
+/* Plan one step of a ragged batch over a latent cache.  Arguments, checks
+ * and errors as pd_plan (same page table rules); any qo <= kv is accepted
+ * (qo > 1: several new tokens, e.g. multi-token prediction).  Work: blocks
+ * of 64 query rows (16 per wavefront) of one request over a chunk of keys;
+ * a request's rows are token-major (row n = token n / H, head n % H).
+ * Chunks of one (request, row group) are merged afterwards; the blocks of
+ * one key chunk are dispatched to the same XCD so that its L2 serves the
+ * second read.  pd_plan_get_stats: decode_units = blocks, decode_row_groups
+ * = (request, 64-row group) pairs, decode_kv_bytes = latent rows read once
+ * per request.  Use pd_plan_workspace_bytes / pd_plan_upload /
+ * pd_plan_free / pd_plan_work_items (kind 1: blocks {request, row group,
+ * key begin, key end, partial slot or -1, 0,0,0}; kind 2: merge groups
+ * {request, row group, first slot, slots}).  Errors: as pd_plan;
+ * PD_ERR_UNSUPPORTED for kv_lora_rank != 512, qk_rope_dim != 64, heads not
+ * a multiple of 16 in [16, 128], other page sizes or dtypes. */
+pd_status pd_mla_plan(const pd_mla_desc* desc, int32_t batch,
+                      const int32_t* qo_lens, const int32_t* kv_lens,
+                      const int32_t* page_indptr, const int32_t* page_indices,
+                      int32_t num_pool_pages, const pd_plan_options* opts,
+                      pd_plan_t* out);
+
+/* Write each request's new latent rows (rows_new, token-major) at positions
+ * [kv - qo, kv) of its pages (post, section "KV Messenger": cache entries
+ * are appended before attention reads them).  Bit-exact copy.
+ * Errors: PD_ERR_INVALID_ARG (null argument, not an MLA plan). */
+pd_status pd_mla_kv_append(pd_plan_t plan, void* d_ws, void* kv_pool,
+                           const void* rows_new, void* stream);
+
+/* Attention of every query row over its request's latent cache, then the
+ * merge of split chunks (fixed order: bitwise reproducible for a fixed
+ * plan).  lse may be NULL.  Errors: PD_ERR_INVALID_ARG (null argument, not
+ * an MLA plan), PD_ERR_HIP. */
+pd_status pd_mla_attention_run(pd_plan_t plan, void* d_ws, const void* q,
+                               const void* kv_pool, float* out, float* lse,
+                               void* stream);
+
+/* Copy whole latent pages (list order) into one contiguous buffer
+ * [n][page bytes], and back into (other) page ids.  Every rank holds the
+ * same latent pages, so a page travels whole from any one rank (post,
+ * section "Sharded KV Cache Transfers").  Arguments and errors as
+ * pd_kv_pack / pd_kv_unpack (buf_bytes >= n * pd_mla_page_bytes). */
+pd_status pd_mla_kv_pack(const pd_mla_desc* desc, const void* kv_pool,
+                         int32_t num_pool_pages, const int32_t* page_ids,
+                         int32_t n, void* d_buf, size_t buf_bytes,
+                         void* d_scratch, size_t scratch_bytes, void* stream);
+pd_status pd_mla_kv_unpack(const pd_mla_desc* desc, void* kv_pool,
+                           int32_t num_pool_pages, const int32_t* page_ids,
+                           int32_t n, const void* d_buf, size_t buf_bytes,
+                           void* d_scratch, size_t scratch_bytes,
+                           void* stream);
 
 /* Static text for a status code. */
 const char* pd_status_string(pd_status s);
