@@ -30,6 +30,10 @@ def command(out: str):
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # packed fp32 VALU forms are kept out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # matrix-product results in architectural registers: the MLA
+            # kernel keeps its query operand in the accumulation registers
+            # (the attention kernels' code is the same either way)
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
             *SOURCES, "-o", out]
 

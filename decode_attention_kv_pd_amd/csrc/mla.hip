@@ -47,6 +47,13 @@ static_assert(MlaCfg::LOADS == 36 && MlaCfg::LOADS_PER_WAVE == 9, "stage loads s
 static_assert(MlaCfg::LDS_BYTES <= 160 * 1024, "LDS of one block");
 static_assert(Lds<128>::RPB == 4 && Lds<64>::RPB == 8, "tile geometry");
 
+// Direct global->LDS load of 16 bytes per lane from a wave-uniform base plus
+// a 32-bit lane offset (the scalar-base form of the load; see load_lds16).
+__device__ __forceinline__ void load_lds16_sbase(const char* base, uint32_t off, LDS_AS char* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
+
 // Page id of key `key` of a request (clamped to its last key).
 __device__ __forceinline__ int mla_page(const MlaParams& p, const ReqInfo& ri, int key) {
   return ldc(p.page_indices + ri.page_start + (min(key, ri.kv - 1) >> p.ps_shift));
@@ -64,6 +71,22 @@ __device__ __forceinline__ void mla_issue(const MlaParams& p, const ReqInfo& ri,
   const int kvm1 = ri.kv - 1;
   const int psm = p.ps - 1;
   constexpr int64_t RB = 2 * kMlaWidth;  // bytes per cache row
+  if (b + 32 <= ri.kv) {
+    // every row valid: keys b .. b + 15 are consecutive slots of page pgA and
+    // b + 16 .. b + 31 of page pgB, so each load is a wave-uniform base plus
+    // a loop-invariant lane offset (the scalar-base form of the load)
+    const char* baseA = pool + ((int64_t)pgA * p.ps + (b & psm)) * RB;
+    const char* baseB = pool + ((int64_t)pgB * p.ps + ((b + 16) & psm)) * RB;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q4 = i / 2, jb = w + 4 * (i % 2);
+      const uint32_t off = (4 * w + Lds<128>::dma_row(lane)) * RB + 256 * q4 + 16 * Lds<128>::dma_chunk(lane);
+      load_lds16_sbase(i % 2 ? baseB : baseA, off, st + q4 * MlaCfg::QUARTER + jb * Lds<128>::BLOCK);
+    }
+    const uint32_t off = (8 * (w % 2) + Lds<64>::dma_row(lane)) * RB + 2 * kMlaLatent + 16 * Lds<64>::dma_chunk(lane);
+    load_lds16_sbase(w < 2 ? baseA : baseB, off, st + MlaCfg::ROPE + w * Lds<64>::BLOCK);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int q4 = i / 2, jb = w + 4 * (i % 2);
@@ -89,6 +112,102 @@ struct MlaLanes {
   int v_off;    // ... of the transposed value reads
 };
 
+// 16-byte LDS read issued from inline asm, so that the compiler neither
+// reorders it nor waits for it: the caller waits with lgkm_wait_for.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16_asm(const LDS_AS char* p) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(p), "n"(OFF) : "memory");
+  return v;
+}
+
+// Wait until the LDS read that produced `v` has landed, given that LATER
+// reads were issued after it.  LDS reads complete in issue order, so at most
+// LATER outstanding LGKM operations means this one is done, whatever else
+// (scalar loads) is in flight.  Tying `v` to the wait keeps its consumer
+// after it.
+template <int LATER>
+__device__ __forceinline__ void lgkm_wait_for(u32x4& v) {
+  static_assert(LATER >= 0 && LATER < 16, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(LATER));
+}
+
+// The score products of one step as a software pipeline: read r (k-step
+// r / 2, keys 16 (r % 2) + (lane & 15)) is issued RING reads ahead of
+// product r, which accumulates into chain r % 2.
+struct MlaSPipe {
+  static constexpr int NR = 2 * (kMlaWidth / 32);
+  static constexpr int RING = 8;
+  template <int R>
+  static constexpr int off() {  // immediate offset of read R from the lane's latent / rotary base
+    return (R / 2) < 16 ? (R % 2) * (16 / Lds<128>::RPB) * Lds<128>::BLOCK + ((R / 2) / 4) * Lds<128>::bytes(32) +
+                              Lds<128>::chunk_step(2 * ((R / 2) % 4))
+                        : (R % 2) * (16 / Lds<64>::RPB) * Lds<64>::BLOCK + Lds<64>::chunk_step(2 * ((R / 2) - 16));
+  }
+};
+
+// Transposed 8-byte LDS read issued from inline asm (see lds_read16_asm).
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr16_asm(const LDS_AS char* p) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(p), "n"(OFF) : "memory");
+  return v;
+}
+
+// The value products of one step: product m (latent entries 128 (m / 8) +
+// 16 (m % 8) ..) takes two transposed reads (keys 4q + e and 16 + 4q + e);
+// the reads of product m + AHEAD are issued before product m waits for its
+// own.  The first AHEAD products' reads are issued before the softmax.
+struct MlaPVPipe {
+  static constexpr int N = kMlaLatent / 16;
+  static constexpr int AHEAD = 7;
+  static constexpr int RING = AHEAD + 1;
+  template <int M, int H>
+  static constexpr int off() {
+    return (M / 8) * Lds<128>::bytes(32) + Lds<128>::chunk_step(M % 8) + H * (16 / Lds<128>::RPB) * Lds<128>::BLOCK;
+  }
+};
+
+template <int M>
+__device__ __forceinline__ void mla_pv_issue(u32x2 (&va)[MlaPVPipe::RING][2], const LDS_AS char* vp) {
+  va[M % MlaPVPipe::RING][0] = lds_read_tr16_asm<MlaPVPipe::off<M, 0>()>(vp);
+  va[M % MlaPVPipe::RING][1] = lds_read_tr16_asm<MlaPVPipe::off<M, 1>()>(vp);
+}
+
+template <int M>
+__device__ __forceinline__ void mla_pv_prologue(u32x2 (&va)[MlaPVPipe::RING][2], const LDS_AS char* vp) {
+  mla_pv_issue<M>(va, vp);
+  if constexpr (M + 1 < MlaPVPipe::AHEAD) mla_pv_prologue<M + 1>(va, vp);
+}
+
+template <int M>
+__device__ __forceinline__ void mla_pv_pipe(u32x2 (&va)[MlaPVPipe::RING][2], const LDS_AS char* vp, u32x4 pb,
+                                            f32x4 (&oacc)[kMlaLatent / 16]) {
+  constexpr int N = MlaPVPipe::N, AHEAD = MlaPVPipe::AHEAD, RING = MlaPVPipe::RING;
+  if constexpr (M + AHEAD < N) mla_pv_issue<M + AHEAD>(va, vp);
+  constexpr int LATER = 2 * ((N - 1 - M) < AHEAD ? (N - 1 - M) : AHEAD);
+  static_assert(LATER < 16, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(va[M % RING][0]), "+v"(va[M % RING][1]) : "n"(LATER));
+  const u32x4 a = {va[M % RING][0][0], va[M % RING][0][1], va[M % RING][1][0], va[M % RING][1][1]};
+  oacc[M] = mfma16(a, pb, oacc[M]);
+  if constexpr (M + 1 < N) mla_pv_pipe<M + 1>(va, vp, pb, oacc);
+}
+
+template <int R>
+__device__ __forceinline__ void mla_s_pipe(u32x4 (&kf)[MlaSPipe::RING], f32x4 (&s)[2], const u32x4 (&qf)[kMlaWidth / 32],
+                                           const LDS_AS char* kl, const LDS_AS char* kr) {
+  constexpr int NR = MlaSPipe::NR, RING = MlaSPipe::RING;
+  if constexpr (R >= RING) {
+    constexpr int i = R - RING;
+    lgkm_wait_for<(NR - 1 - i < RING - 1) ? NR - 1 - i : RING - 1>(kf[i % RING]);
+    s[i % 2] = mfma16(kf[i % RING], qf[i / 2], s[i % 2]);
+  }
+  if constexpr (R < NR) kf[R % RING] = lds_read16_asm<MlaSPipe::off<R>()>((R / 2) < 16 ? kl : kr);
+  if constexpr (R + 1 < NR + RING) mla_s_pipe<R + 1>(kf, s, qf, kl, kr);
+}
+
 // One 32-key step of a wavefront's 16 rows from stage `st`: S^T = K Q^T
 // (K 16 bytes per lane from LDS, Q^T in registers), the speculative online
 // softmax per column, then O^T += V^T P^T with V^T read transposed from the
@@ -98,20 +217,15 @@ __device__ __forceinline__ void mla_step(const MlaParams& p, const LDS_AS char* 
                                          const u32x4 (&qf)[MlaCfg::KS], float& m_ref, f32x4& lacc,
                                          f32x4 (&oacc)[MlaCfg::DB]) {
   const float cl = p.c_log2;
-  f32x4 s[2];
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    const LDS_AS char* kp = st + ln.k_lat + sb * (16 / Lds<128>::RPB) * Lds<128>::BLOCK;
-    s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks)
-      s[sb] = mfma16(lds_read16(kp + (ks / 4) * MlaCfg::QUARTER + Lds<128>::chunk_step(2 * (ks % 4))), qf[ks],
-                     s[sb]);
-    const LDS_AS char* rp = st + ln.k_rope + sb * (16 / Lds<64>::RPB) * Lds<64>::BLOCK;
-#pragma unroll
-    for (int ks = 16; ks < MlaCfg::KS; ++ks)
-      s[sb] = mfma16(lds_read16(rp + Lds<64>::chunk_step(2 * (ks - 16))), qf[ks], s[sb]);
-  }
+  // S^T: the two 16-key chains interleaved; operand read r feeds product r
+  // (k-step r / 2, keys 16 (r % 2) ..).  With one wavefront per SIMD nothing
+  // else hides the LDS latency, so the reads run RING ahead of the products.
+  f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  u32x4 kf[MlaSPipe::RING];
+  mla_s_pipe<0>(kf, s, qf, st + ln.k_lat, st + ln.k_rope);
+  u32x2 va[MlaPVPipe::RING][2];
+  const LDS_AS char* vp = st + ln.v_off;
+  mla_pv_prologue<0>(va, vp);  // the first value reads land during the softmax
   if (b + 32 > lim) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -152,18 +266,8 @@ __device__ __forceinline__ void mla_step(const MlaParams& p, const LDS_AS char* 
   }
   const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
   lacc = mfma16(u32x4{kBf16OnesPair, kBf16OnesPair, kBf16OnesPair, kBf16OnesPair}, pb, lacc);
-  // V^T[d = 128 q4 + 16 db + (lane & 15)][keys 4q + e, 16 + 4q + e]
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const LDS_AS char* vp = st + q4 * MlaCfg::QUARTER + ln.v_off;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const u32x2 a1 = lds_read_tr16(vp + Lds<128>::chunk_step(db));
-      const u32x2 a2 = lds_read_tr16(vp + Lds<128>::chunk_step(db) + (16 / Lds<128>::RPB) * Lds<128>::BLOCK);
-      const u32x4 a = {a1[0], a1[1], a2[0], a2[1]};
-      oacc[8 * q4 + db] = mfma16(a, pb, oacc[8 * q4 + db]);
-    }
-  }
+  // V^T[d = 16 m + (lane & 15)][keys 4q + e, 16 + 4q + e]
+  mla_pv_pipe<0>(va, vp, pb, oacc);
 }
 
 // Wait until at most n of this wavefront's stage loads are in flight.
@@ -192,18 +296,32 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_kernel(MlaParams p) {
 
   MlaLanes ln;
   ln.q = lane >> 4;
-  ln.k_lat = Lds<128>::off(lane & 15, (lane >> 4) & 1) + 32 * (lane >> 5);
-  ln.k_rope = MlaCfg::ROPE + Lds<64>::off(lane & 15, (lane >> 4) & 1) + 32 * (lane >> 5);
+  // Lane group g = lane / 16 of the score operands carries entries 8 g .. +7
+  // of each 32-entry k-step (chunk g of its four).
+  const int kchunk = lane >> 4;
+  ln.k_lat = Lds<128>::off(lane & 15, kchunk & 1) + Lds<128>::chunk_step(kchunk >> 1);
+  ln.k_rope = MlaCfg::ROPE + Lds<64>::off(lane & 15, kchunk & 1) + Lds<64>::chunk_step(kchunk >> 1);
   {
     const int j = lane & 15;
     ln.v_off = Lds<128>::off(4 * ln.q + (j >> 2), (j & 3) >> 1) + 8 * (j & 1);
   }
 
+  // Q^T fragments, loaded before any stage load, into accumulation registers
+  // (a read-only MFMA operand; the architectural registers hold O^T and the
+  // operand ring).  The loads are issued from inline asm: the compiler would
+  // otherwise place a wait for them at their first use inside the step loop
+  // (vmcnt(0), which also drains every stage load in flight, at every step).
+  // They are older than all stage loads, so the loop's own wait for step 0
+  // covers them.
   u32x4 qf[MlaCfg::KS];
-  {
-    const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)(ri.qo_start + t) * H + h) * kMlaWidth + 8 * ln.q;
+  if (active) {
+    const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)(ri.qo_start + t) * H + h) * kMlaWidth + 8 * kchunk;
 #pragma unroll
-    for (int ks = 0; ks < MlaCfg::KS; ++ks) qf[ks] = active ? *(const u32x4*)(qp + 32 * ks) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < MlaCfg::KS; ++ks)
+      asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(qf[ks]) : "v"(qp + 32 * ks) : "memory");
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < MlaCfg::KS; ++ks) qf[ks] = u32x4{0, 0, 0, 0};
   }
   f32x4 oacc[MlaCfg::DB];
 #pragma unroll
@@ -249,31 +367,36 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_kernel(MlaParams p) {
   for (int db = 0; db < MlaCfg::DB; ++db) *(f32x4*)(po + 16 * db + 4 * ln.q) = oacc[db] * inv;
 }
 
-// Log-sum-exp merge of the partial results of one (request, row group), in
-// part order (deterministic for a fixed plan).
+// Log-sum-exp merge of split partial results: one wavefront per query row
+// of a merge group (lanes over the 512 latent entries, 8 each), parts in
+// slot order (deterministic for a fixed plan).
 __global__ __launch_bounds__(kMlaThreads) void mla_merge_kernel(MlaParams p) {
-  const MlaMergeGroup mg = ldc(p.mg + blockIdx.x);
+  const int wg = blockIdx.x * kMlaWaves + uniform_i(threadIdx.x >> 6);
+  const int gi = wg / kMlaRows, n = wg % kMlaRows;
+  if (gi >= p.n_mg) return;
+  const MlaMergeGroup mg = ldc(p.mg + gi);
   const ReqInfo ri = ldc(p.req + mg.req);
-  const int nrows = min(kMlaRows, ri.qo * p.H - kMlaRows * mg.rg);
-  constexpr int D4 = kMlaLatent / 4;
-  for (int idx = threadIdx.x; idx < nrows * D4; idx += kMlaThreads) {
-    const int n = idx / D4, d4 = idx % D4;
-    float mx = -INFINITY;
-    for (int i = 0; i < mg.nparts; ++i) mx = fmaxf(mx, p.part_lse[(int64_t)(mg.part0 + i) * kMlaRows + n]);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float sw = 0.f;
-    for (int i = 0; i < mg.nparts; ++i) {
-      const int64_t slot = (int64_t)(mg.part0 + i) * kMlaRows + n;
-      const float li = p.part_lse[slot];
-      const float wi = (li == -INFINITY) ? 0.f : __expf(li - mx);
-      acc += *(const f32x4*)(p.part_o + slot * kMlaLatent + 4 * d4) * wi;
-      sw += wi;
-    }
-    const int rn = kMlaRows * mg.rg + n;
-    const int64_t row = (int64_t)(ri.qo_start + rn / p.H) * p.H + rn % p.H;
-    *(f32x4*)(p.out + row * kMlaLatent + 4 * d4) = acc * (1.f / sw);
-    if (d4 == 0 && p.lse) p.lse[row] = mx + __logf(sw);
+  const int rn = kMlaRows * mg.rg + n;  // row of the request (token rn / H, head rn % H)
+  if (rn >= ri.qo * p.H) return;
+  const int lane = threadIdx.x & 63;
+  float mx = -INFINITY;
+  for (int i = 0; i < mg.nparts; ++i) mx = fmaxf(mx, ldc(p.part_lse + (int64_t)(mg.part0 + i) * kMlaRows + n));
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  float sw = 0.f;
+  for (int i = 0; i < mg.nparts; ++i) {
+    const int64_t slot = (int64_t)(mg.part0 + i) * kMlaRows + n;
+    const float li = ldc(p.part_lse + slot);
+    const float wi = (li == -INFINITY) ? 0.f : __expf(li - mx);
+    const float* po = p.part_o + slot * kMlaLatent + 4 * lane;
+    a0 += *(const f32x4*)po * wi;
+    a1 += *(const f32x4*)(po + 256) * wi;
+    sw += wi;
   }
+  const int64_t row = (int64_t)(ri.qo_start + rn / p.H) * p.H + rn % p.H;
+  const float inv = 1.f / sw;
+  *(f32x4*)(p.out + row * kMlaLatent + 4 * lane) = a0 * inv;
+  *(f32x4*)(p.out + row * kMlaLatent + 256 + 4 * lane) = a1 * inv;
+  if (lane == 0 && p.lse) p.lse[row] = mx + __logf(sw);
 }
 
 // Append: one wavefront per new token row; 72 16-byte copies of its latent
@@ -302,7 +425,9 @@ hipError_t launch_mla(const MlaParams& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.n_mg > 0) hipLaunchKernelGGL(mla_merge_kernel, dim3(p.n_mg), dim3(kMlaThreads), 0, s, p);
+  if (p.n_mg > 0)
+    hipLaunchKernelGGL(mla_merge_kernel, dim3((p.n_mg * kMlaRows + kMlaWaves - 1) / kMlaWaves), dim3(kMlaThreads), 0,
+                       s, p);
   return hipGetLastError();
 }
 
