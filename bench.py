@@ -62,6 +62,7 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the interference / chunked-prefill sweep")
     ap.add_argument("--sweep-decodes", type=int, default=32, help="decodes in the 1PnD sweep batches")
+    ap.add_argument("--no-mla", action="store_true", help="skip the latent-cache (MLA) decode legs")
     ap.add_argument("--cpu-decode-requests", type=int, default=24)
     ap.add_argument("--cpu-prefill-tokens", type=int, default=16)
     return ap.parse_args()
@@ -318,6 +319,78 @@ def interference_sweep(args, pd, torch):
     return res
 
 
+def mla_legs(args, pd, torch):
+    """Latent-cache (MLA) decode legs, untimed by the step: the two DeepSeek
+    decode workloads (one TP-8 rank with 16 query heads, one data-parallel
+    attention rank with 128; 64 requests, caches of 1024..8192 tokens, page
+    size 64, pools drawn on the device).  Per workload: pd_mla_kv_append of
+    the 64 new latent rows, pd_mla_attention_run (attention + merge), and
+    pd_mla_kv_pack / pd_mla_kv_unpack of the longest request's pages.
+    Algorithmic work: latent rows read once per request + Q read + O and LSE
+    written (bytes); 2 (576 + 512) flops per (query row, visible key)."""
+    from workloads import device_normal_, device_seed, make_mla_batch
+
+    reps = args.phase_reps * 4
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    res = {}
+    for name in ("mla_tp8", "mla_dp"):
+        b = make_mla_batch(name, materialize=False)
+        pool = device_normal_(torch.empty(b.pool_shape, dtype=torch.bfloat16, device="cuda"), device_seed(b.wid, 0, 0))
+        n = int(b.qo_indptr[-1])
+        q = device_normal_(torch.empty((n, b.H, b.width), dtype=torch.bfloat16, device="cuda"), device_seed(b.wid, 0, 1))
+        rows_new = device_normal_(torch.empty((n, b.width), dtype=torch.bfloat16, device="cuda"), device_seed(b.wid, 0, 2))
+        d = pd.make_mla_desc(b.H, b.ps, b.causal, b.sm_scale)
+        plan = pd.pd_mla_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages)
+        ws = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device="cuda")
+        pd.pd_plan_upload(plan, ws)
+        out = torch.empty((n, b.H, b.d_c), dtype=torch.float32, device="cuda")
+        lse = torch.empty((n, b.H), dtype=torch.float32, device="cuda")
+        t_app = timed(lambda: pd.pd_mla_kv_append(plan, ws, pool, rows_new))
+        t_attn = timed(lambda: pd.pd_mla_attention_run(plan, ws, q, pool, out, lse))
+        keys = int(b.kv_lens.astype(np.int64).sum())
+        nbytes = keys * b.width * 2 + n * b.H * (b.width * 2 + b.d_c * 4 + 4)
+        flops = keys * b.H * 2 * (b.width + b.d_c)           # qo = 1: every cached key is visible
+        ideal = max(nbytes / (PEAK_HBM_GBPS * 1e9), flops / (PEAK_BF16_TFLOPS * 1e12))
+        r = int(np.argmax(b.kv_lens))
+        ids = b.request_pages(r)
+        pb = pd.pd_mla_page_bytes(d)
+        buf = torch.empty(len(ids) * pb, dtype=torch.uint8, device="cuda")
+        scr = torch.empty(4 * len(ids), dtype=torch.uint8, device="cuda")
+        t_pack = timed(lambda: pd.pd_mla_kv_pack(d, pool, b.num_pool_pages, ids, buf, scr))
+        t_unpack = timed(lambda: pd.pd_mla_kv_unpack(d, pool, b.num_pool_pages, ids, buf, scr))
+        st = plan.stats()
+        res[name] = {
+            "shape": f"B {b.B}, H {b.H}, latent {b.d_c} + rotary {b.d_r}, page {b.ps}, bf16, kv 1024..8192",
+            "attention_ms": round(t_attn, 4), "blocks": st.decode_units, "chunk_keys": st.decode_chunk_keys,
+            "GBps": round(nbytes / (t_attn * 1e-3) / 1e9, 1),
+            "TFLOPs": round(flops / (t_attn * 1e-3) / 1e12, 1),
+            "hbm_frac": round(nbytes / (t_attn * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "mfma_frac": round(flops / (t_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "roofline_frac": round(ideal / (t_attn * 1e-3), 4),
+            "append_us": round(t_app * 1e3, 2),
+            "pack_pages": len(ids), "pack_GBps": round(2 * len(ids) * pb / (t_pack * 1e-3) / 1e9, 1),
+            "unpack_GBps": round(2 * len(ids) * pb / (t_unpack * 1e-3) / 1e9, 1),
+        }
+        plan.close()
+        del pool, q, rows_new, out, lse, ws, buf, scr
+    torch.cuda.synchronize()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -497,6 +570,10 @@ def main():
     if not args.no_transfers:
         result["transfers"] = transfer_legs(args, pd, torch, b, desc, pool, pack_ids, unpack_ids)
         print(f"[bench] transfer legs done", file=sys.stderr, flush=True)
+
+    if not args.no_mla:
+        result["mla_decode"] = mla_legs(args, pd, torch)
+        print(f"[bench] MLA legs done", file=sys.stderr, flush=True)
 
     if not args.no_sweep:
         result["interference_sweep"] = interference_sweep(args, pd, torch)
