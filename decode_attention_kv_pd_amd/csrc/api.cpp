@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <new>
 #include <string>
@@ -105,6 +106,7 @@ struct pd_plan_s {
   // latent-cache (MLA) plans: pd_mla_plan fills these instead of pf / du / mg
   bool mla = false;
   pd_mla_desc mdesc{};
+  int32_t mla_waves = 4, mla_rows = 64;  // MLA blocks: wavefronts, query rows
   std::vector<pdk::MlaItem> mitems;  // launch order
   std::vector<pdk::MlaMergeGroup> mmg;
   size_t off_mitems = 0, off_mmg = 0;
@@ -442,15 +444,79 @@ pdk::AttnParams attn_params(const pd_plan_s& P, void* d_ws) {
 // multiple of 32 keys) so that about two blocks per CU exist; the blocks of
 // one (request, chunk) read the same cache rows and are placed on one XCD,
 // one dispatch round apart (block i runs on XCD i % 8), longest first.
+// Keys of the chunks a request of kv keys splits into at a chunk length of
+// about `chunk`: equal lengths, multiples of 32.
+int mla_chunk_len(int kv, int chunk) {
+  const int nch = (kv + chunk - 1) / chunk;
+  return ((kv + nch - 1) / nch + 31) / 32 * 32;
+}
+
+// Chunk length for an MLA plan. A block stages the whole latent row once per
+// 32-key step for all its query rows, holds one CU (its LDS ring takes most of
+// the 160 KB) and writes R x 513 floats per partial, which the merge reads
+// back. The cost of a candidate is the greedy (longest first) makespan of its
+// blocks over one block slot per CU, each block charged its keys plus a fixed
+// start-up and drain cost, plus the partial traffic spread over the chip. The
+// constants are in units of one key step of one block, fitted to MI355X runs
+// of 64 requests x U{1024..8192} keys at 16 and 128 heads.
+int mla_pick_chunk(const pd_plan_s& P, int R, int num_cus) {
+  constexpr double kBlockKeys = 96.0;    // Q load, ring fill, partial store
+  const double part_keys = R / 100.0;    // R x 513 x 4 B written, then read by the merge
+  int max_kv = 0;
+  for (int r = 0; r < P.B; ++r)
+    if (P.req[r].qo > 0) max_kv = std::max(max_kv, P.req[r].kv);
+  const int top = std::max(256, std::min(16384, (max_kv + 127) / 128 * 128));
+  std::vector<int> cand;
+  for (double c = 256; c < top * 1.2; c *= 1.125) {
+    const int v = std::min(top, ((int)c + 127) / 128 * 128);
+    if (cand.empty() || cand.back() != v) cand.push_back(v);
+  }
+  int best = top;
+  double best_cost = -1;
+  std::vector<int> blk;
+  for (int chunk : cand) {
+    blk.clear();
+    int64_t parts = 0;
+    for (int r = 0; r < P.B; ++r) {
+      const pdk::ReqInfo& ri = P.req[r];
+      if (ri.qo == 0) continue;
+      const int ng = (int)(((int64_t)ri.qo * P.mdesc.num_qo_heads + R - 1) / R);
+      const int len = mla_chunk_len(ri.kv, chunk);
+      const int nch = (ri.kv + len - 1) / len;
+      if (nch > 1) parts += (int64_t)ng * nch;
+      for (int c = 0; c < nch; ++c)
+        for (int g = 0; g < ng; ++g) blk.push_back(std::min(ri.kv, (c + 1) * len) - c * len);
+    }
+    if (blk.size() > (size_t)64 * num_cus && chunk != top) continue;  // far past one CU each
+    std::sort(blk.begin(), blk.end(), std::greater<int>());
+    std::vector<double> slot(std::min<size_t>(num_cus, blk.size()), 0.0);  // min-heap of CU finish times
+    double span = 0;
+    for (int k : blk) {
+      std::pop_heap(slot.begin(), slot.end(), std::greater<double>());
+      slot.back() += k + kBlockKeys;
+      span = std::max(span, slot.back());
+      std::push_heap(slot.begin(), slot.end(), std::greater<double>());
+    }
+    const double cost = span + parts * part_keys;
+    if (best_cost < 0 || cost < best_cost) best_cost = cost, best = chunk;
+  }
+  return best;
+}
+
 pd_status build_mla_plan(pd_plan_s& P, const pd_plan_options* opts) {
   const pd_mla_desc& d = P.mdesc;
   const int H = d.num_qo_heads;
   const int num_cus = (opts && opts->num_cus > 0) ? opts->num_cus : 256;
+  // 128 heads fill an 8-wavefront block (two per SIMD) with one token's rows,
+  // so each cache step is staged once for all of them; fewer heads use 4.
+  P.mla_waves = H >= 128 ? 8 : 4;
+  P.mla_rows = 16 * P.mla_waves;
+  const int R = P.mla_rows;
   int64_t work = 0;  // row groups x keys
   for (int r = 0; r < P.B; ++r) {
     const pdk::ReqInfo& ri = P.req[r];
     if (ri.qo == 0) continue;
-    const int ng = (int)(((int64_t)ri.qo * H + pdk::kMlaRows - 1) / pdk::kMlaRows);
+    const int ng = (int)(((int64_t)ri.qo * H + R - 1) / R);
     work += (int64_t)ng * ri.kv;
     P.decode_bytes += (int64_t)ri.kv * pdk::kMlaWidth * 2;
   }
@@ -458,9 +524,7 @@ pd_status build_mla_plan(pd_plan_s& P, const pd_plan_options* opts) {
   if (opts && opts->decode_chunk_keys > 0) {
     chunk = (opts->decode_chunk_keys + 31) / 32 * 32;
   } else if (work > 0) {
-    int64_t c = (work + 2LL * num_cus - 1) / (2LL * num_cus);
-    c = (c + 127) / 128 * 128;
-    chunk = (int)std::min<int64_t>(std::max<int64_t>(c, 256), 16384);
+    chunk = mla_pick_chunk(P, R, num_cus);
   }
   P.chunk_keys = chunk;
   struct Task {  // one (request, chunk): its row groups' blocks
@@ -471,11 +535,9 @@ pd_status build_mla_plan(pd_plan_s& P, const pd_plan_options* opts) {
   for (int r = 0; r < P.B; ++r) {
     const pdk::ReqInfo& ri = P.req[r];
     if (ri.qo == 0) continue;
-    const int ng = (int)(((int64_t)ri.qo * H + pdk::kMlaRows - 1) / pdk::kMlaRows);
-    int nch = (ri.kv + chunk - 1) / chunk;
-    int len = (ri.kv + nch - 1) / nch;
-    len = (len + 31) / 32 * 32;
-    nch = (ri.kv + len - 1) / len;
+    const int ng = (int)(((int64_t)ri.qo * H + R - 1) / R);
+    const int len = mla_chunk_len(ri.kv, chunk);
+    const int nch = (ri.kv + len - 1) / len;
     nchunks[r] = nch;
     if (nch > 1) {  // slots [base, base + ng * nch): row group rg's chunk c at base + rg * nch + c
       base[r] = P.n_parts;
@@ -524,9 +586,9 @@ pd_status build_mla_plan(pd_plan_s& P, const pd_plan_options* opts) {
   off = align_up(off + sizeof(pdk::MlaMergeGroup) * P.mmg.size());
   P.meta_bytes = off;
   P.off_part_o = off;
-  off = align_up(off + sizeof(float) * (size_t)P.n_parts * pdk::kMlaRows * pdk::kMlaLatent);
+  off = align_up(off + sizeof(float) * (size_t)P.n_parts * R * pdk::kMlaLatent);
   P.off_part_lse = off;
-  off = align_up(off + sizeof(float) * (size_t)P.n_parts * pdk::kMlaRows);
+  off = align_up(off + sizeof(float) * (size_t)P.n_parts * R);
   P.ws_bytes = off;
   P.blob.assign(P.meta_bytes, 0);
   auto put = [&](size_t o, const void* src, size_t n) {
@@ -554,6 +616,8 @@ pdk::MlaParams mla_params(const pd_plan_s& P, void* d_ws) {
   a.n_mg = (int32_t)P.mmg.size();
   a.B = P.B;
   a.total_rows = P.total_rows;
+  a.waves = P.mla_waves;
+  a.rows = P.mla_rows;
   a.H = P.mdesc.num_qo_heads;
   a.ps = P.mdesc.page_size;
   a.ps_shift = __builtin_ctz((unsigned)P.mdesc.page_size);
@@ -732,7 +796,7 @@ pd_status pd_plan_get_stats(pd_plan_t plan, pd_plan_stats* out) {
   if (plan->mla) {
     int32_t groups = 0;
     for (const auto& ri : plan->req)
-      groups += (int32_t)(((int64_t)ri.qo * plan->mdesc.num_qo_heads + pdk::kMlaRows - 1) / pdk::kMlaRows);
+      groups += (int32_t)(((int64_t)ri.qo * plan->mdesc.num_qo_heads + plan->mla_rows - 1) / plan->mla_rows);
     out->decode_row_groups = groups;
   } else {
     out->decode_row_groups = (int32_t)plan->mg.size();

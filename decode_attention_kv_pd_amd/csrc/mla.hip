@@ -24,8 +24,8 @@
 namespace pdk {
 namespace {
 
-// A block: 4 wavefronts, 16 query rows each (the N index of both products),
-// one key range, 32 keys per step.  A step's rows are staged in LDS as four
+// A block: 4 or 8 wavefronts (NW), 16 query rows each (the N index of both
+// products), one key range, 32 keys per step.  A step's rows are staged in LDS as four
 // Lds<128> tiles (the latent entries 0-127, 128-255, 256-383, 384-511) and
 // one Lds<64> tile (the rotary key), the layout whose 16-byte reads (score
 // operand) and transposed reads (value operand) are bank-conflict free at
@@ -41,9 +41,11 @@ struct MlaCfg {
   static constexpr int DB = kMlaLatent / 16;                    // 16-row d-blocks of O^T
   static constexpr int LAT_LOADS = 4 * (KEYS / Lds<128>::RPB);  // 1 KiB block loads of a step (latent)
   static constexpr int LOADS = LAT_LOADS + KEYS / Lds<64>::RPB; // ... and rotary
-  static constexpr int LOADS_PER_WAVE = LOADS / kMlaWaves;
+  // block loads of wavefront w per step: 4 wavefronts take 8 latent + 1
+  // rotary each; 8 wavefronts take 4 latent each, and 0-3 one rotary more
+  __device__ static constexpr int loads(int nw, int w) { return nw == 4 ? 9 : (w < 4 ? 5 : 4); }
 };
-static_assert(MlaCfg::LOADS == 36 && MlaCfg::LOADS_PER_WAVE == 9, "stage loads split over the wavefronts");
+static_assert(MlaCfg::LAT_LOADS == 32 && MlaCfg::LOADS == 36, "stage loads split over the wavefronts");
 static_assert(MlaCfg::LDS_BYTES <= 160 * 1024, "LDS of one block");
 static_assert(Lds<128>::RPB == 4 && Lds<64>::RPB == 8, "tile geometry");
 
@@ -59,12 +61,15 @@ __device__ __forceinline__ int mla_page(const MlaParams& p, const ReqInfo& ri, i
   return ldc(p.page_indices + ri.page_start + (min(key, ri.kv - 1) >> p.ps_shift));
 }
 
-// Wavefront w's share (9 of the 36 block loads) of the step at key b into
-// stage `st`: latent loads i = 0..7 (tile i / 2, rows 4 (w + 4 (i % 2)) ..
-// +3), then one rotary load (rows 8 w .. + 7).  pgA / pgB are the pages of
-// keys b .. b + 15 and b + 16 .. b + 31 (pages hold >= 16 aligned keys).
-// Keys >= kv (only in a request's last step) are read from key kv - 1
-// instead: finite data, masked later, and tail slots are never read.
+// Wavefront w's share of the 36 block loads of the step at key b into stage
+// `st`.  4 wavefronts: latent loads i = 0..7 (tile i / 2, rows 4 (w + 4 (i %
+// 2)) .. +3), then one rotary load (rows 8 w .. +7).  8 wavefronts: latent
+// loads i = 0..3 (tile i, rows 4 w .. +3), and wavefronts 0-3 one rotary
+// load (rows 8 w .. +7).  pgA / pgB are the pages of keys b .. b + 15 and
+// b + 16 .. b + 31 (pages hold >= 16 aligned keys).  Keys >= kv (only in a
+// request's last step) are read from key kv - 1 instead: finite data, masked
+// later, and tail slots are never read.
+template <int NW>
 __device__ __forceinline__ void mla_issue(const MlaParams& p, const ReqInfo& ri, int b, int pgA, int pgB,
                                           int w, int lane, LDS_AS char* st) {
   const char* pool = (const char*)p.pool;
@@ -78,25 +83,27 @@ __device__ __forceinline__ void mla_issue(const MlaParams& p, const ReqInfo& ri,
     const char* baseA = pool + ((int64_t)pgA * p.ps + (b & psm)) * RB;
     const char* baseB = pool + ((int64_t)pgB * p.ps + ((b + 16) & psm)) * RB;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q4 = i / 2, jb = w + 4 * (i % 2);
-      const uint32_t off = (4 * w + Lds<128>::dma_row(lane)) * RB + 256 * q4 + 16 * Lds<128>::dma_chunk(lane);
-      load_lds16_sbase(i % 2 ? baseB : baseA, off, st + q4 * MlaCfg::QUARTER + jb * Lds<128>::BLOCK);
+    for (int i = 0; i < (NW == 4 ? 8 : 4); ++i) {
+      const int q4 = NW == 4 ? i / 2 : i, jb = NW == 4 ? w + 4 * (i % 2) : w;
+      const uint32_t off = (4 * (jb % 4) + Lds<128>::dma_row(lane)) * RB + 256 * q4 + 16 * Lds<128>::dma_chunk(lane);
+      load_lds16_sbase(jb >= 4 ? baseB : baseA, off, st + q4 * MlaCfg::QUARTER + jb * Lds<128>::BLOCK);
     }
-    const uint32_t off = (8 * (w % 2) + Lds<64>::dma_row(lane)) * RB + 2 * kMlaLatent + 16 * Lds<64>::dma_chunk(lane);
-    load_lds16_sbase(w < 2 ? baseA : baseB, off, st + MlaCfg::ROPE + w * Lds<64>::BLOCK);
+    if (NW == 4 || w < 4) {
+      const uint32_t off = (8 * (w % 2) + Lds<64>::dma_row(lane)) * RB + 2 * kMlaLatent + 16 * Lds<64>::dma_chunk(lane);
+      load_lds16_sbase(w < 2 ? baseA : baseB, off, st + MlaCfg::ROPE + w * Lds<64>::BLOCK);
+    }
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int q4 = i / 2, jb = w + 4 * (i % 2);
+  for (int i = 0; i < (NW == 4 ? 8 : 4); ++i) {
+    const int q4 = NW == 4 ? i / 2 : i, jb = NW == 4 ? w + 4 * (i % 2) : w;
     const int row = 4 * jb + Lds<128>::dma_row(lane);
     const int key = min(b + row, kvm1);
     const int page = jb < 4 ? pgA : pgB;
     load_lds16(pool + ((int64_t)page * p.ps + (key & psm)) * RB + 256 * q4 + 16 * Lds<128>::dma_chunk(lane),
                st + q4 * MlaCfg::QUARTER + jb * Lds<128>::BLOCK);
   }
-  {
+  if (NW == 4 || w < 4) {
     const int row = 8 * w + Lds<64>::dma_row(lane);
     const int key = min(b + row, kvm1);
     const int page = w < 2 ? pgA : pgB;
@@ -136,9 +143,10 @@ __device__ __forceinline__ void lgkm_wait_for(u32x4& v) {
 // The score products of one step as a software pipeline: read r (k-step
 // r / 2, keys 16 (r % 2) + (lane & 15)) is issued RING reads ahead of
 // product r, which accumulates into chain r % 2.
+template <int RING_>
 struct MlaSPipe {
   static constexpr int NR = 2 * (kMlaWidth / 32);
-  static constexpr int RING = 8;
+  static constexpr int RING = RING_;
   template <int R>
   static constexpr int off() {  // immediate offset of read R from the lane's latent / rotary base
     return (R / 2) < 16 ? (R % 2) * (16 / Lds<128>::RPB) * Lds<128>::BLOCK + ((R / 2) / 4) * Lds<128>::bytes(32) +
@@ -160,9 +168,10 @@ __device__ __forceinline__ u32x2 lds_read_tr16_asm(const LDS_AS char* p) {
 // 16 (m % 8) ..) takes two transposed reads (keys 4q + e and 16 + 4q + e);
 // the reads of product m + AHEAD are issued before product m waits for its
 // own.  The first AHEAD products' reads are issued before the softmax.
+template <int AHEAD_>
 struct MlaPVPipe {
   static constexpr int N = kMlaLatent / 16;
-  static constexpr int AHEAD = 7;
+  static constexpr int AHEAD = AHEAD_;
   static constexpr int RING = AHEAD + 1;
   template <int M, int H>
   static constexpr int off() {
@@ -170,42 +179,42 @@ struct MlaPVPipe {
   }
 };
 
-template <int M>
-__device__ __forceinline__ void mla_pv_issue(u32x2 (&va)[MlaPVPipe::RING][2], const LDS_AS char* vp) {
-  va[M % MlaPVPipe::RING][0] = lds_read_tr16_asm<MlaPVPipe::off<M, 0>()>(vp);
-  va[M % MlaPVPipe::RING][1] = lds_read_tr16_asm<MlaPVPipe::off<M, 1>()>(vp);
+template <int AHEAD, int M>
+__device__ __forceinline__ void mla_pv_issue(u32x2 (&va)[AHEAD + 1][2], const LDS_AS char* vp) {
+  va[M % (AHEAD + 1)][0] = lds_read_tr16_asm<MlaPVPipe<AHEAD>::template off<M, 0>()>(vp);
+  va[M % (AHEAD + 1)][1] = lds_read_tr16_asm<MlaPVPipe<AHEAD>::template off<M, 1>()>(vp);
 }
 
-template <int M>
-__device__ __forceinline__ void mla_pv_prologue(u32x2 (&va)[MlaPVPipe::RING][2], const LDS_AS char* vp) {
-  mla_pv_issue<M>(va, vp);
-  if constexpr (M + 1 < MlaPVPipe::AHEAD) mla_pv_prologue<M + 1>(va, vp);
+template <int AHEAD, int M>
+__device__ __forceinline__ void mla_pv_prologue(u32x2 (&va)[AHEAD + 1][2], const LDS_AS char* vp) {
+  mla_pv_issue<AHEAD, M>(va, vp);
+  if constexpr (M + 1 < AHEAD) mla_pv_prologue<AHEAD, M + 1>(va, vp);
 }
 
-template <int M>
-__device__ __forceinline__ void mla_pv_pipe(u32x2 (&va)[MlaPVPipe::RING][2], const LDS_AS char* vp, u32x4 pb,
+template <int AHEAD, int M>
+__device__ __forceinline__ void mla_pv_pipe(u32x2 (&va)[AHEAD + 1][2], const LDS_AS char* vp, u32x4 pb,
                                             f32x4 (&oacc)[kMlaLatent / 16]) {
-  constexpr int N = MlaPVPipe::N, AHEAD = MlaPVPipe::AHEAD, RING = MlaPVPipe::RING;
-  if constexpr (M + AHEAD < N) mla_pv_issue<M + AHEAD>(va, vp);
+  constexpr int N = MlaPVPipe<AHEAD>::N, RING = AHEAD + 1;
+  if constexpr (M + AHEAD < N) mla_pv_issue<AHEAD, M + AHEAD>(va, vp);
   constexpr int LATER = 2 * ((N - 1 - M) < AHEAD ? (N - 1 - M) : AHEAD);
   static_assert(LATER < 16, "lgkmcnt field");
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(va[M % RING][0]), "+v"(va[M % RING][1]) : "n"(LATER));
   const u32x4 a = {va[M % RING][0][0], va[M % RING][0][1], va[M % RING][1][0], va[M % RING][1][1]};
   oacc[M] = mfma16(a, pb, oacc[M]);
-  if constexpr (M + 1 < N) mla_pv_pipe<M + 1>(va, vp, pb, oacc);
+  if constexpr (M + 1 < N) mla_pv_pipe<AHEAD, M + 1>(va, vp, pb, oacc);
 }
 
-template <int R>
-__device__ __forceinline__ void mla_s_pipe(u32x4 (&kf)[MlaSPipe::RING], f32x4 (&s)[2], const u32x4 (&qf)[kMlaWidth / 32],
+template <int RING, int R>
+__device__ __forceinline__ void mla_s_pipe(u32x4 (&kf)[RING], f32x4 (&s)[2], const u32x4 (&qf)[kMlaWidth / 32],
                                            const LDS_AS char* kl, const LDS_AS char* kr) {
-  constexpr int NR = MlaSPipe::NR, RING = MlaSPipe::RING;
+  constexpr int NR = MlaSPipe<RING>::NR;
   if constexpr (R >= RING) {
     constexpr int i = R - RING;
     lgkm_wait_for<(NR - 1 - i < RING - 1) ? NR - 1 - i : RING - 1>(kf[i % RING]);
     s[i % 2] = mfma16(kf[i % RING], qf[i / 2], s[i % 2]);
   }
-  if constexpr (R < NR) kf[R % RING] = lds_read16_asm<MlaSPipe::off<R>()>((R / 2) < 16 ? kl : kr);
-  if constexpr (R + 1 < NR + RING) mla_s_pipe<R + 1>(kf, s, qf, kl, kr);
+  if constexpr (R < NR) kf[R % RING] = lds_read16_asm<MlaSPipe<RING>::template off<R>()>((R / 2) < 16 ? kl : kr);
+  if constexpr (R + 1 < NR + RING) mla_s_pipe<RING, R + 1>(kf, s, qf, kl, kr);
 }
 
 // One 32-key step of a wavefront's 16 rows from stage `st`: S^T = K Q^T
@@ -213,6 +222,7 @@ __device__ __forceinline__ void mla_s_pipe(u32x4 (&kf)[MlaSPipe::RING], f32x4 (&
 // softmax per column, then O^T += V^T P^T with V^T read transposed from the
 // latent tiles.  Key order inside the step is permuted identically in P^T
 // and V^T (keys 4q + e and 16 + 4q + e in lane group q).
+template <int SRING, int PVAHEAD>
 __device__ __forceinline__ void mla_step(const MlaParams& p, const LDS_AS char* st, int b, int lim, MlaLanes ln,
                                          const u32x4 (&qf)[MlaCfg::KS], float& m_ref, f32x4& lacc,
                                          f32x4 (&oacc)[MlaCfg::DB]) {
@@ -221,11 +231,11 @@ __device__ __forceinline__ void mla_step(const MlaParams& p, const LDS_AS char* 
   // (k-step r / 2, keys 16 (r % 2) ..).  With one wavefront per SIMD nothing
   // else hides the LDS latency, so the reads run RING ahead of the products.
   f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  u32x4 kf[MlaSPipe::RING];
-  mla_s_pipe<0>(kf, s, qf, st + ln.k_lat, st + ln.k_rope);
-  u32x2 va[MlaPVPipe::RING][2];
+  u32x4 kf[SRING];
+  mla_s_pipe<SRING, 0>(kf, s, qf, st + ln.k_lat, st + ln.k_rope);
+  u32x2 va[PVAHEAD + 1][2];
   const LDS_AS char* vp = st + ln.v_off;
-  mla_pv_prologue<0>(va, vp);  // the first value reads land during the softmax
+  mla_pv_prologue<PVAHEAD, 0>(va, vp);  // the first value reads land during the softmax
   if (b + 32 > lim) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -267,20 +277,26 @@ __device__ __forceinline__ void mla_step(const MlaParams& p, const LDS_AS char* 
   const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
   lacc = mfma16(u32x4{kBf16OnesPair, kBf16OnesPair, kBf16OnesPair, kBf16OnesPair}, pb, lacc);
   // V^T[d = 16 m + (lane & 15)][keys 4q + e, 16 + 4q + e]
-  mla_pv_pipe<0>(va, vp, pb, oacc);
+  mla_pv_pipe<PVAHEAD, 0>(va, vp, pb, oacc);
 }
 
-// Wait until at most n of this wavefront's stage loads are in flight.
+// Wait for this wavefront's loads of the current step, with `later_steps`
+// (<= 2) later steps' loads (LPW each) still allowed in flight.
+template <int LPW>
 __device__ __forceinline__ void mla_wait_loads(int later_steps) {
   if (later_steps >= 2)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * MlaCfg::LOADS_PER_WAVE) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW) : "memory");
   else if (later_steps == 1)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(MlaCfg::LOADS_PER_WAVE) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-__global__ __launch_bounds__(kMlaThreads, 1) void mla_kernel(MlaParams p) {
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
+  // 4 wavefronts: one per SIMD, deep operand-read rings; 8 wavefronts: two
+  // per SIMD (256 registers each), shallower rings
+  constexpr int SRING = NW == 4 ? 8 : 4, PVAHEAD = NW == 4 ? 7 : 2;
   __shared__ __attribute__((aligned(16))) char lds_raw[MlaCfg::LDS_BYTES];
   LDS_AS char* lds = (LDS_AS char*)lds_raw;
   const MlaItem it = ldc(p.items + blockIdx.x);
@@ -288,7 +304,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_kernel(MlaParams p) {
   const int lane = threadIdx.x & 63;
   const int w = uniform_i(threadIdx.x >> 6);
   const int H = p.H;
-  const int n0 = kMlaRows * it.rg + 16 * w;  // first query row of this wavefront (H is a multiple of 16)
+  const int n0 = 16 * NW * it.rg + 16 * w;  // first query row of this wavefront (H is a multiple of 16)
   const bool active = n0 < ri.qo * H;
   const int t = active ? n0 / H : 0;
   const int h = n0 % H + (lane & 15);
@@ -334,19 +350,24 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_kernel(MlaParams p) {
   for (int s = 0; s < 3; ++s)
     if (s < nsteps) {
       const int b = it.k0 + 32 * s;
-      mla_issue(p, ri, b, mla_page(p, ri, b), mla_page(p, ri, b + 16), w, lane, lds + s * MlaCfg::STAGE);
+      mla_issue<NW>(p, ri, b, mla_page(p, ri, b), mla_page(p, ri, b + 16), w, lane, lds + s * MlaCfg::STAGE);
     }
   int pgA = mla_page(p, ri, it.k0 + 96), pgB = mla_page(p, ri, it.k0 + 112);  // step 3
   for (int i = 0; i < nsteps; ++i) {
-    mla_wait_loads(nsteps - 1 - i);
+    if (MlaCfg::loads(NW, w) == 9)
+      mla_wait_loads<9>(nsteps - 1 - i);
+    else if (MlaCfg::loads(NW, w) == 5)
+      mla_wait_loads<5>(nsteps - 1 - i);
+    else
+      mla_wait_loads<4>(nsteps - 1 - i);
     __syncthreads();  // step i visible to all; stage (i + 3) % 4 = (i - 1) % 4 read by all
     if (i + 3 < nsteps) {
-      mla_issue(p, ri, it.k0 + 32 * (i + 3), pgA, pgB, w, lane, lds + ((i + 3) & 3) * MlaCfg::STAGE);
+      mla_issue<NW>(p, ri, it.k0 + 32 * (i + 3), pgA, pgB, w, lane, lds + ((i + 3) & 3) * MlaCfg::STAGE);
       pgA = mla_page(p, ri, it.k0 + 32 * (i + 4));
       pgB = mla_page(p, ri, it.k0 + 32 * (i + 4) + 16);
     }
     const int b = it.k0 + 32 * i;
-    if (active && b < lim) mla_step(p, lds + (i & 3) * MlaCfg::STAGE, b, lim, ln, qf, m_ref, lacc, oacc);
+    if (active && b < lim) mla_step<SRING, PVAHEAD>(p, lds + (i & 3) * MlaCfg::STAGE, b, lim, ln, qf, m_ref, lacc, oacc);
   }
 
   if (!active) return;
@@ -359,7 +380,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_kernel(MlaParams p) {
     po = p.out + row * kMlaLatent;
     if (ln.q == 0 && p.lse) p.lse[row] = lse;
   } else {
-    const int64_t slot = (int64_t)it.part * kMlaRows + 16 * w + (lane & 15);
+    const int64_t slot = (int64_t)it.part * (16 * NW) + 16 * w + (lane & 15);
     po = p.part_o + slot * kMlaLatent;
     if (ln.q == 0) p.part_lse[slot] = lse;
   }
@@ -370,21 +391,22 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_kernel(MlaParams p) {
 // Log-sum-exp merge of split partial results: one wavefront per query row
 // of a merge group (lanes over the 512 latent entries, 8 each), parts in
 // slot order (deterministic for a fixed plan).
-__global__ __launch_bounds__(kMlaThreads) void mla_merge_kernel(MlaParams p) {
-  const int wg = blockIdx.x * kMlaWaves + uniform_i(threadIdx.x >> 6);
-  const int gi = wg / kMlaRows, n = wg % kMlaRows;
+__global__ __launch_bounds__(64 * kMlaMergeWaves) void mla_merge_kernel(MlaParams p) {
+  const int wg = blockIdx.x * kMlaMergeWaves + uniform_i(threadIdx.x >> 6);
+  const int R = p.rows;
+  const int gi = wg / R, n = wg % R;
   if (gi >= p.n_mg) return;
   const MlaMergeGroup mg = ldc(p.mg + gi);
   const ReqInfo ri = ldc(p.req + mg.req);
-  const int rn = kMlaRows * mg.rg + n;  // row of the request (token rn / H, head rn % H)
+  const int rn = R * mg.rg + n;  // row of the request (token rn / H, head rn % H)
   if (rn >= ri.qo * p.H) return;
   const int lane = threadIdx.x & 63;
   float mx = -INFINITY;
-  for (int i = 0; i < mg.nparts; ++i) mx = fmaxf(mx, ldc(p.part_lse + (int64_t)(mg.part0 + i) * kMlaRows + n));
+  for (int i = 0; i < mg.nparts; ++i) mx = fmaxf(mx, ldc(p.part_lse + (int64_t)(mg.part0 + i) * R + n));
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
   float sw = 0.f;
   for (int i = 0; i < mg.nparts; ++i) {
-    const int64_t slot = (int64_t)(mg.part0 + i) * kMlaRows + n;
+    const int64_t slot = (int64_t)(mg.part0 + i) * R + n;
     const float li = ldc(p.part_lse + slot);
     const float wi = (li == -INFINITY) ? 0.f : __expf(li - mx);
     const float* po = p.part_o + slot * kMlaLatent + 4 * lane;
@@ -421,13 +443,16 @@ __global__ __launch_bounds__(64) void mla_append_kernel(MlaParams p, void* pool,
 
 hipError_t launch_mla(const MlaParams& p, hipStream_t s) {
   if (p.n_items > 0) {
-    hipLaunchKernelGGL(mla_kernel, dim3(p.n_items), dim3(kMlaThreads), 0, s, p);
+    if (p.waves == 8)
+      hipLaunchKernelGGL(mla_kernel<8>, dim3(p.n_items), dim3(512), 0, s, p);
+    else
+      hipLaunchKernelGGL(mla_kernel<4>, dim3(p.n_items), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.n_mg > 0)
-    hipLaunchKernelGGL(mla_merge_kernel, dim3((p.n_mg * kMlaRows + kMlaWaves - 1) / kMlaWaves), dim3(kMlaThreads), 0,
-                       s, p);
+    hipLaunchKernelGGL(mla_merge_kernel, dim3((p.n_mg * p.rows + kMlaMergeWaves - 1) / kMlaMergeWaves),
+                       dim3(64 * kMlaMergeWaves), 0, s, p);
   return hipGetLastError();
 }
 

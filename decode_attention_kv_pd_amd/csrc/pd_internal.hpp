@@ -101,13 +101,14 @@ struct XferParams {
 constexpr int kMlaLatent = 512;
 constexpr int kMlaRope = 64;
 constexpr int kMlaWidth = kMlaLatent + kMlaRope;
-constexpr int kMlaWaves = 4;                   // wavefronts per block
-constexpr int kMlaThreads = 64 * kMlaWaves;
-constexpr int kMlaRows = 16 * kMlaWaves;       // query rows per block (16 per wavefront)
+// Blocks of the MLA kernel have 4 or 8 wavefronts of 16 query rows each
+// (64 or 128 rows; a plan uses one width, MlaParams::waves).
+constexpr int kMlaMergeWaves = 4;              // wavefronts per block of the merge kernel
 
-// One block of the MLA kernel: query rows [64 rg, 64 rg + 64) of request
-// `req` (row n = token n / H, head n % H) over keys [k0, k1).  part >= 0:
-// the partial result goes to slot `part`; part < 0: straight to out / lse.
+// One block of the MLA kernel: query rows [R rg, R rg + R) of request `req`
+// (R = 16 * waves rows; row n = token n / H, head n % H) over keys [k0, k1).
+// part >= 0: the partial result goes to slot `part`; part < 0: straight to
+// out / lse.
 struct MlaItem {
   int32_t req, rg, k0, k1, part, rsv0, rsv1, rsv2;
 };
@@ -127,9 +128,10 @@ struct MlaParams {
   const int32_t* page_indices;
   const MlaItem* items;
   const MlaMergeGroup* mg;
-  float* part_o;      // [n_parts][kMlaRows][kMlaLatent]
-  float* part_lse;    // [n_parts][kMlaRows]
+  float* part_o;      // [n_parts][rows][kMlaLatent]
+  float* part_lse;    // [n_parts][rows]
   int32_t n_items, n_mg, B, total_rows;
+  int32_t waves, rows;  // wavefronts per block (4 or 8), query rows per block (16 waves)
   int32_t H, ps, ps_shift, causal;
   float sm_scale;
   float c_log2;       // sm_scale * log2(e)

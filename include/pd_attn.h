@@ -441,12 +441,13 @@ size_t pd_mla_page_bytes(const pd_mla_desc* desc);
 /* Plan one step of a ragged batch over a latent cache.  Arguments, checks
  * and errors as pd_plan (same page table rules); any qo <= kv is accepted
  * (qo > 1: several new tokens, e.g. multi-token prediction).  Work: blocks
- * of 64 query rows (16 per wavefront) of one request over a chunk of keys;
+ * of 16 query rows per wavefront (8 wavefronts, 128 rows, at 128 heads or
+ * more; 4 wavefronts, 64 rows, below) of one request over a chunk of keys;
  * a request's rows are token-major (row n = token n / H, head n % H).
  * Chunks of one (request, row group) are merged afterwards; the blocks of
  * one key chunk are dispatched to the same XCD so that its L2 serves the
  * second read.  pd_plan_get_stats: decode_units = blocks, decode_row_groups
- * = (request, 64-row group) pairs, decode_kv_bytes = latent rows read once
+ * = (request, row group) pairs, decode_kv_bytes = latent rows read once
  * per request.  Use pd_plan_workspace_bytes / pd_plan_upload /
  * pd_plan_free / pd_plan_work_items (kind 1: blocks {request, row group,
  * key begin, key end, partial slot or -1, 0,0,0}; kind 2: merge groups

@@ -57,16 +57,21 @@ def test_plan_rejects_bad_batches():
     expect("PD_ERR_INVALID_ARG", pd.pd_mla_plan, d, [-1], [5], [0, 1], [0], 4)
 
 
+def rows_per_block(H):
+    """Query rows per block: 8 wavefronts of 16 rows at 128 heads, else 4."""
+    return 128 if H >= 128 else 64
+
+
 def check_cover(b, plan):
-    """Every (request, 64-row group) has its keys [0, kv) covered exactly once
+    """Every (request, row group) has its keys [0, kv) covered exactly once
     by its blocks; split groups use distinct partial slots that their merge
     group lists in chunk order, unsplit groups write straight to out."""
     items, mg = plan.work_items(1), plan.work_items(2)
-    H = b.H
+    H, R = b.H, rows_per_block(b.H)
     groups = {}
     for req, rg, k0, k1, part, *_ in items.tolist():
         groups.setdefault((req, rg), []).append((k0, k1, part))
-    want = {(r, g) for r in range(b.B) for g in range(-(-int(b.qo_lens[r]) * H // 64))}
+    want = {(r, g) for r in range(b.B) for g in range(-(-int(b.qo_lens[r]) * H // R))}
     assert set(groups) == want
     mgs = {(r, g): (p0, n) for r, g, p0, n in mg.tolist()}
     used = set()
@@ -105,17 +110,17 @@ def test_plan_figures():
     p = plan_of(b)
     s = p.stats()
     assert s.decode_kv_bytes == int(b.kv_lens.astype(np.int64).sum()) * 576 * 2
-    assert s.decode_row_groups == 2 * b.B and s.prefill_tiles == 0
+    assert s.decode_row_groups == b.B and s.prefill_tiles == 0   # 128 heads: one 128-row group
     assert s.decode_units == len(p.work_items(1))
     n_parts = int(p.work_items(2)[:, 3].sum())
-    assert p.workspace_bytes >= n_parts * 64 * (512 + 1) * 4
+    assert p.workspace_bytes >= n_parts * 128 * (512 + 1) * 4
 
 
 def test_blocks_of_one_key_chunk_share_an_xcd():
-    """With 128 heads each key chunk of a request is read by two blocks; in
-    a balanced batch they sit one dispatch round apart on the same XCD
-    (block i runs on XCD i % 8)."""
-    b = make_mla_batch("mla_dp", materialize=False, lengths=([1] * 64, [4096] * 64))
+    """With two new tokens of 128 heads (two 128-row groups) each key chunk
+    of a request is read by two blocks; in a balanced batch they sit one
+    dispatch round apart on the same XCD (block i runs on XCD i % 8)."""
+    b = make_mla_batch("mla_dp", materialize=False, lengths=([2] * 64, [4096] * 64))
     items = plan_of(b, decode_chunk_keys=1024).work_items(1)
     pos = {}
     for i, (req, rg, k0, *_rest) in enumerate(items.tolist()):
