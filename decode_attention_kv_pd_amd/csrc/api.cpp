@@ -507,10 +507,10 @@ pd_status build_mla_plan(pd_plan_s& P, const pd_plan_options* opts) {
   const pd_mla_desc& d = P.mdesc;
   const int H = d.num_qo_heads;
   const int num_cus = (opts && opts->num_cus > 0) ? opts->num_cus : 256;
-  // 128 heads fill an 8-wavefront block (two per SIMD) with one token's rows,
-  // so each cache step is staged once for all of them; fewer heads use 4.
-  P.mla_waves = H >= 128 ? 8 : 4;
-  P.mla_rows = 16 * P.mla_waves;
+  // 128 heads: one token's rows fill a block of 4 wavefronts x 32 rows, so
+  // each cache step is staged once for all of them; fewer heads: 4 x 16.
+  P.mla_waves = 4;
+  P.mla_rows = H == 128 ? 128 : 64;  // H is a multiple of 16 in [16, 128]
   const int R = P.mla_rows;
   int64_t work = 0;  // row groups x keys
   for (int r = 0; r < P.B; ++r) {

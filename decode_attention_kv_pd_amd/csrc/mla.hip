@@ -11,7 +11,8 @@
 // i.e. one-KV-head attention whose key is the whole cache row (576 bf16) and
 // whose value is the row's first 512 entries.  Every query head of a request
 // reads the same rows, so one block serves 64 query rows of a request and
-// stages each 32-key step of the cache once for all of them.
+// stages each 32-key step of the cache once for all of them.  (Requests of
+// 128 heads use mla_wide.hip: 32 rows per wavefront, 128 per block.)
 //
 // Layout (see include/pd_attn.h): pool [pages][ps][576] bf16 (latent then
 // rotary key), q [rows][H][576] bf16, out fp32 [rows][H][512], lse [rows][H].
@@ -19,98 +20,11 @@
 #include <stdint.h>
 
 #include "device_common.hpp"
+#include "mla_common.hpp"
 #include "pd_internal.hpp"
 
 namespace pdk {
 namespace {
-
-// A block: 4 or 8 wavefronts (NW), 16 query rows each (the N index of both
-// products), one key range, 32 keys per step.  A step's rows are staged in LDS as four
-// Lds<128> tiles (the latent entries 0-127, 128-255, 256-383, 384-511) and
-// one Lds<64> tile (the rotary key), the layout whose 16-byte reads (score
-// operand) and transposed reads (value operand) are bank-conflict free at
-// 128 columns.  Four stages are in flight.
-struct MlaCfg {
-  static constexpr int KEYS = 32;
-  static constexpr int QUARTER = Lds<128>::bytes(KEYS);
-  static constexpr int ROPE = 4 * QUARTER;
-  static constexpr int STAGE = ROPE + Lds<64>::bytes(KEYS);
-  static constexpr int NSTAGE = 4;
-  static constexpr int LDS_BYTES = NSTAGE * STAGE;
-  static constexpr int KS = kMlaWidth / 32;                     // 32-wide k-steps of S (16 latent, 2 rotary)
-  static constexpr int DB = kMlaLatent / 16;                    // 16-row d-blocks of O^T
-  static constexpr int LAT_LOADS = 4 * (KEYS / Lds<128>::RPB);  // 1 KiB block loads of a step (latent)
-  static constexpr int LOADS = LAT_LOADS + KEYS / Lds<64>::RPB; // ... and rotary
-  // block loads of wavefront w per step: 4 wavefronts take 8 latent + 1
-  // rotary each; 8 wavefronts take 4 latent each, and 0-3 one rotary more
-  __device__ static constexpr int loads(int nw, int w) { return nw == 4 ? 9 : (w < 4 ? 5 : 4); }
-};
-static_assert(MlaCfg::LAT_LOADS == 32 && MlaCfg::LOADS == 36, "stage loads split over the wavefronts");
-static_assert(MlaCfg::LDS_BYTES <= 160 * 1024, "LDS of one block");
-static_assert(Lds<128>::RPB == 4 && Lds<64>::RPB == 8, "tile geometry");
-
-// Direct global->LDS load of 16 bytes per lane from a wave-uniform base plus
-// a 32-bit lane offset (the scalar-base form of the load; see load_lds16).
-__device__ __forceinline__ void load_lds16_sbase(const char* base, uint32_t off, LDS_AS char* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
-}
-
-// Page id of key `key` of a request (clamped to its last key).
-__device__ __forceinline__ int mla_page(const MlaParams& p, const ReqInfo& ri, int key) {
-  return ldc(p.page_indices + ri.page_start + (min(key, ri.kv - 1) >> p.ps_shift));
-}
-
-// Wavefront w's share of the 36 block loads of the step at key b into stage
-// `st`.  4 wavefronts: latent loads i = 0..7 (tile i / 2, rows 4 (w + 4 (i %
-// 2)) .. +3), then one rotary load (rows 8 w .. +7).  8 wavefronts: latent
-// loads i = 0..3 (tile i, rows 4 w .. +3), and wavefronts 0-3 one rotary
-// load (rows 8 w .. +7).  pgA / pgB are the pages of keys b .. b + 15 and
-// b + 16 .. b + 31 (pages hold >= 16 aligned keys).  Keys >= kv (only in a
-// request's last step) are read from key kv - 1 instead: finite data, masked
-// later, and tail slots are never read.
-template <int NW>
-__device__ __forceinline__ void mla_issue(const MlaParams& p, const ReqInfo& ri, int b, int pgA, int pgB,
-                                          int w, int lane, LDS_AS char* st) {
-  const char* pool = (const char*)p.pool;
-  const int kvm1 = ri.kv - 1;
-  const int psm = p.ps - 1;
-  constexpr int64_t RB = 2 * kMlaWidth;  // bytes per cache row
-  if (b + 32 <= ri.kv) {
-    // every row valid: keys b .. b + 15 are consecutive slots of page pgA and
-    // b + 16 .. b + 31 of page pgB, so each load is a wave-uniform base plus
-    // a loop-invariant lane offset (the scalar-base form of the load)
-    const char* baseA = pool + ((int64_t)pgA * p.ps + (b & psm)) * RB;
-    const char* baseB = pool + ((int64_t)pgB * p.ps + ((b + 16) & psm)) * RB;
-#pragma unroll
-    for (int i = 0; i < (NW == 4 ? 8 : 4); ++i) {
-      const int q4 = NW == 4 ? i / 2 : i, jb = NW == 4 ? w + 4 * (i % 2) : w;
-      const uint32_t off = (4 * (jb % 4) + Lds<128>::dma_row(lane)) * RB + 256 * q4 + 16 * Lds<128>::dma_chunk(lane);
-      load_lds16_sbase(jb >= 4 ? baseB : baseA, off, st + q4 * MlaCfg::QUARTER + jb * Lds<128>::BLOCK);
-    }
-    if (NW == 4 || w < 4) {
-      const uint32_t off = (8 * (w % 2) + Lds<64>::dma_row(lane)) * RB + 2 * kMlaLatent + 16 * Lds<64>::dma_chunk(lane);
-      load_lds16_sbase(w < 2 ? baseA : baseB, off, st + MlaCfg::ROPE + w * Lds<64>::BLOCK);
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < (NW == 4 ? 8 : 4); ++i) {
-    const int q4 = NW == 4 ? i / 2 : i, jb = NW == 4 ? w + 4 * (i % 2) : w;
-    const int row = 4 * jb + Lds<128>::dma_row(lane);
-    const int key = min(b + row, kvm1);
-    const int page = jb < 4 ? pgA : pgB;
-    load_lds16(pool + ((int64_t)page * p.ps + (key & psm)) * RB + 256 * q4 + 16 * Lds<128>::dma_chunk(lane),
-               st + q4 * MlaCfg::QUARTER + jb * Lds<128>::BLOCK);
-  }
-  if (NW == 4 || w < 4) {
-    const int row = 8 * w + Lds<64>::dma_row(lane);
-    const int key = min(b + row, kvm1);
-    const int page = w < 2 ? pgA : pgB;
-    load_lds16(pool + ((int64_t)page * p.ps + (key & psm)) * RB + 2 * kMlaLatent + 16 * Lds<64>::dma_chunk(lane),
-               st + MlaCfg::ROPE + w * Lds<64>::BLOCK);
-  }
-}
 
 struct MlaLanes {
   int q;        // 16-lane group
@@ -118,27 +32,6 @@ struct MlaLanes {
   int k_rope;   // ... of the rotary score-operand reads
   int v_off;    // ... of the transposed value reads
 };
-
-// 16-byte LDS read issued from inline asm, so that the compiler neither
-// reorders it nor waits for it: the caller waits with lgkm_wait_for.
-template <int OFF>
-__device__ __forceinline__ u32x4 lds_read16_asm(const LDS_AS char* p) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
-  u32x4 v;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(p), "n"(OFF) : "memory");
-  return v;
-}
-
-// Wait until the LDS read that produced `v` has landed, given that LATER
-// reads were issued after it.  LDS reads complete in issue order, so at most
-// LATER outstanding LGKM operations means this one is done, whatever else
-// (scalar loads) is in flight.  Tying `v` to the wait keeps its consumer
-// after it.
-template <int LATER>
-__device__ __forceinline__ void lgkm_wait_for(u32x4& v) {
-  static_assert(LATER >= 0 && LATER < 16, "lgkmcnt field");
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(LATER));
-}
 
 // The score products of one step as a software pipeline: read r (k-step
 // r / 2, keys 16 (r % 2) + (lane & 15)) is issued RING reads ahead of
@@ -154,15 +47,6 @@ struct MlaSPipe {
                         : (R % 2) * (16 / Lds<64>::RPB) * Lds<64>::BLOCK + Lds<64>::chunk_step(2 * ((R / 2) - 16));
   }
 };
-
-// Transposed 8-byte LDS read issued from inline asm (see lds_read16_asm).
-template <int OFF>
-__device__ __forceinline__ u32x2 lds_read_tr16_asm(const LDS_AS char* p) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
-  u32x2 v;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(p), "n"(OFF) : "memory");
-  return v;
-}
 
 // The value products of one step: product m (latent entries 128 (m / 8) +
 // 16 (m % 8) ..) takes two transposed reads (keys 4q + e and 16 + 4q + e);
@@ -280,23 +164,9 @@ __device__ __forceinline__ void mla_step(const MlaParams& p, const LDS_AS char* 
   mla_pv_pipe<PVAHEAD, 0>(va, vp, pb, oacc);
 }
 
-// Wait for this wavefront's loads of the current step, with `later_steps`
-// (<= 2) later steps' loads (LPW each) still allowed in flight.
-template <int LPW>
-__device__ __forceinline__ void mla_wait_loads(int later_steps) {
-  if (later_steps >= 2)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW) : "memory");
-  else if (later_steps == 1)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-template <int NW>
-__global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
-  // 4 wavefronts: one per SIMD, deep operand-read rings; 8 wavefronts: two
-  // per SIMD (256 registers each), shallower rings
-  constexpr int SRING = NW == 4 ? 8 : 4, PVAHEAD = NW == 4 ? 7 : 2;
+__global__ __launch_bounds__(256, 1) void mla_kernel(MlaParams p) {
+  // one wavefront per SIMD: deep operand-read rings hide the LDS latency
+  constexpr int SRING = 8, PVAHEAD = 7;
   __shared__ __attribute__((aligned(16))) char lds_raw[MlaCfg::LDS_BYTES];
   LDS_AS char* lds = (LDS_AS char*)lds_raw;
   const MlaItem it = ldc(p.items + blockIdx.x);
@@ -304,7 +174,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   const int lane = threadIdx.x & 63;
   const int w = uniform_i(threadIdx.x >> 6);
   const int H = p.H;
-  const int n0 = 16 * NW * it.rg + 16 * w;  // first query row of this wavefront (H is a multiple of 16)
+  const int n0 = 64 * it.rg + 16 * w;  // first query row of this wavefront (H is a multiple of 16)
   const bool active = n0 < ri.qo * H;
   const int t = active ? n0 / H : 0;
   const int h = n0 % H + (lane & 15);
@@ -350,19 +220,14 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
   for (int s = 0; s < 3; ++s)
     if (s < nsteps) {
       const int b = it.k0 + 32 * s;
-      mla_issue<NW>(p, ri, b, mla_page(p, ri, b), mla_page(p, ri, b + 16), w, lane, lds + s * MlaCfg::STAGE);
+      mla_issue(p, ri, b, mla_page(p, ri, b), mla_page(p, ri, b + 16), w, lane, lds + s * MlaCfg::STAGE);
     }
   int pgA = mla_page(p, ri, it.k0 + 96), pgB = mla_page(p, ri, it.k0 + 112);  // step 3
   for (int i = 0; i < nsteps; ++i) {
-    if (MlaCfg::loads(NW, w) == 9)
-      mla_wait_loads<9>(nsteps - 1 - i);
-    else if (MlaCfg::loads(NW, w) == 5)
-      mla_wait_loads<5>(nsteps - 1 - i);
-    else
-      mla_wait_loads<4>(nsteps - 1 - i);
+    mla_wait_loads<MlaCfg::LOADS_PER_WAVE>(nsteps - 1 - i);
     __syncthreads();  // step i visible to all; stage (i + 3) % 4 = (i - 1) % 4 read by all
     if (i + 3 < nsteps) {
-      mla_issue<NW>(p, ri, it.k0 + 32 * (i + 3), pgA, pgB, w, lane, lds + ((i + 3) & 3) * MlaCfg::STAGE);
+      mla_issue(p, ri, it.k0 + 32 * (i + 3), pgA, pgB, w, lane, lds + ((i + 3) & 3) * MlaCfg::STAGE);
       pgA = mla_page(p, ri, it.k0 + 32 * (i + 4));
       pgB = mla_page(p, ri, it.k0 + 32 * (i + 4) + 16);
     }
@@ -380,7 +245,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_kernel(MlaParams p) {
     po = p.out + row * kMlaLatent;
     if (ln.q == 0 && p.lse) p.lse[row] = lse;
   } else {
-    const int64_t slot = (int64_t)it.part * (16 * NW) + 16 * w + (lane & 15);
+    const int64_t slot = (int64_t)it.part * 64 + 16 * w + (lane & 15);
     po = p.part_o + slot * kMlaLatent;
     if (ln.q == 0) p.part_lse[slot] = lse;
   }
@@ -443,12 +308,14 @@ __global__ __launch_bounds__(64) void mla_append_kernel(MlaParams p, void* pool,
 
 hipError_t launch_mla(const MlaParams& p, hipStream_t s) {
   if (p.n_items > 0) {
-    if (p.waves == 8)
-      hipLaunchKernelGGL(mla_kernel<8>, dim3(p.n_items), dim3(512), 0, s, p);
-    else
-      hipLaunchKernelGGL(mla_kernel<4>, dim3(p.n_items), dim3(256), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (p.rows == 128) {
+      hipError_t e = launch_mla_wide(p, s);  // 32 rows per wavefront (mla_wide.hip)
+      if (e != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL(mla_kernel, dim3(p.n_items), dim3(256), 0, s, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (p.n_mg > 0)
     hipLaunchKernelGGL(mla_merge_kernel, dim3((p.n_mg * p.rows + kMlaMergeWaves - 1) / kMlaMergeWaves),

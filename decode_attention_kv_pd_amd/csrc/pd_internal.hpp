@@ -101,12 +101,13 @@ struct XferParams {
 constexpr int kMlaLatent = 512;
 constexpr int kMlaRope = 64;
 constexpr int kMlaWidth = kMlaLatent + kMlaRope;
-// Blocks of the MLA kernel have 4 or 8 wavefronts of 16 query rows each
-// (64 or 128 rows; a plan uses one width, MlaParams::waves).
+// Blocks of the MLA kernels have 4 wavefronts of 16 query rows (64 rows,
+// mla.hip) or 32 query rows (128 rows, requests of 128 heads, mla_wide.hip);
+// a plan uses one width, MlaParams::rows.
 constexpr int kMlaMergeWaves = 4;              // wavefronts per block of the merge kernel
 
 // One block of the MLA kernel: query rows [R rg, R rg + R) of request `req`
-// (R = 16 * waves rows; row n = token n / H, head n % H) over keys [k0, k1).
+// (R = MlaParams::rows; row n = token n / H, head n % H) over keys [k0, k1).
 // part >= 0: the partial result goes to slot `part`; part < 0: straight to
 // out / lse.
 struct MlaItem {
@@ -131,13 +132,14 @@ struct MlaParams {
   float* part_o;      // [n_parts][rows][kMlaLatent]
   float* part_lse;    // [n_parts][rows]
   int32_t n_items, n_mg, B, total_rows;
-  int32_t waves, rows;  // wavefronts per block (4 or 8), query rows per block (16 waves)
+  int32_t waves, rows;  // wavefronts per block (4); query rows per block (64, or 128 for 128 heads)
   int32_t H, ps, ps_shift, causal;
   float sm_scale;
   float c_log2;       // sm_scale * log2(e)
 };
 
 hipError_t launch_mla(const MlaParams& p, hipStream_t s);
+hipError_t launch_mla_wide(const MlaParams& p, hipStream_t s);  // attention only: 128-row blocks
 hipError_t launch_mla_append(const MlaParams& p, void* pool, const void* rows_new, hipStream_t s);
 
 hipError_t launch_attention(const AttnParams& p, int dtype, hipStream_t s);

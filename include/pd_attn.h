@@ -441,8 +441,8 @@ size_t pd_mla_page_bytes(const pd_mla_desc* desc);
 /* Plan one step of a ragged batch over a latent cache.  Arguments, checks
  * and errors as pd_plan (same page table rules); any qo <= kv is accepted
  * (qo > 1: several new tokens, e.g. multi-token prediction).  Work: blocks
- * of 16 query rows per wavefront (8 wavefronts, 128 rows, at 128 heads or
- * more; 4 wavefronts, 64 rows, below) of one request over a chunk of keys;
+ * of 4 wavefronts over one request's query rows and a chunk of its keys: 32
+ * rows per wavefront (128, one token) at 128 heads, 16 (64 rows) below;
  * a request's rows are token-major (row n = token n / H, head n % H).
  * Chunks of one (request, row group) are merged afterwards; the blocks of
  * one key chunk are dispatched to the same XCD so that its L2 serves the
