@@ -6,8 +6,9 @@ normaliser is the sum of the bf16-rounded softmax weights).
 Cases: the parity workload (kv 1, a two-token step, kv 300); 16 to 128 heads;
 page sizes 16 to 128; ragged lengths with tails; one-, two- and four-token
 steps; non-causal; split-count invariance and bitwise determinism; a
-sharpened softmax and logits rising along the cache (the rescale path); and
-the two full-size decode workloads on sampled requests.  Appends and page
+sharpened softmax and logits rising along the cache (the rescale path), each
+at 128 heads too (the 32-row kernel, whose output lives in accumulation
+registers); and the two full-size decode workloads on sampled requests.  Appends and page
 transfers are checked bit for bit, and NaN-poisoned spare pages and tail
 slots are never read."""
 import functools
@@ -115,6 +116,8 @@ RAGGED = [
     dict(lengths=([1, 2], [2049, 517]), heads=128, page_size=64),
     dict(lengths=([1, 1, 2], [5000, 17, 130]), heads=16, page_size=128),
     dict(lengths=([2, 1, 0, 1], [90, 40, 7, 1]), heads=16, causal=False),
+    dict(lengths=([3, 1], [40, 1]), heads=128, causal=False),
+    dict(lengths=([4, 2, 1], [4, 70, 33]), heads=128, page_size=16),
 ]
 
 
@@ -132,8 +135,9 @@ def test_split_count_invariance(chunk):
     assert np.abs(out1 - out0).max() <= 2 * TOL
 
 
-def test_bitwise_deterministic_for_a_fixed_plan():
-    _, b = batch("mla_tiny", lengths=([1, 1, 2], [4000, 900, 300]), heads=64)
+@pytest.mark.parametrize("heads", [64, 128])
+def test_bitwise_deterministic_for_a_fixed_plan(heads):
+    _, b = batch("mla_tiny", lengths=([1, 1, 2], [4000, 900, 300]), heads=heads)
     run = MlaRun(b, chunk=256)
     first = run.step()
     for _ in range(3):
@@ -141,9 +145,10 @@ def test_bitwise_deterministic_for_a_fixed_plan():
         assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
 
 
-def test_sharpened_softmax():
-    key, b = batch("mla_tiny", lengths=([1, 2, 1], [400, 1000, 33]), heads=32, q_gain=8.0)
-    check(key, b, "mla_sharp")
+@pytest.mark.parametrize("heads", [32, 128])
+def test_sharpened_softmax(heads):
+    key, b = batch("mla_tiny", lengths=([1, 2, 1], [400, 1000, 33]), heads=heads, q_gain=8.0)
+    check(key, b, f"mla_sharp{heads}")
 
 
 def rising(b, nats_per_key):
@@ -160,18 +165,22 @@ def rising(b, nats_per_key):
     return b
 
 
+@pytest.mark.parametrize("heads", [16, 128])
 @pytest.mark.parametrize("nats", [1.0, 0.05])
-def test_rising_logits(nats):
-    key, b = batch("mla_tiny", lengths=([1, 2, 1], [600, 300, 2000]), heads=16, rep=int(nats * 100))
+def test_rising_logits(nats, heads):
+    """The running max moves many times per block: the rescale of the
+    accumulated output (for 128 heads, the accumulation-register path)."""
+    key, b = batch("mla_tiny", lengths=([1, 2, 1], [600, 300, 2000]), heads=heads, rep=int(nats * 100))
     rising(b, nats)
     oracle.cache_clear()
-    check(key, b, f"mla_rising{nats}")
+    check(key, b, f"mla_rising{nats}_h{heads}")
 
 
-def test_one_dominant_key_is_reproduced():
+@pytest.mark.parametrize("heads", [16, 128])
+def test_one_dominant_key_is_reproduced(heads):
     """One key whose logit is 60 nats above the rest: O equals its latent row
     (bf16 values, exactly representable) to fp32 rounding."""
-    key, b = batch("mla_tiny", lengths=([1], [777]), heads=16, rep=5)
+    key, b = batch("mla_tiny", lengths=([1], [777]), heads=heads, rep=5)
     q = bf16_bits_to_f32(b.q).copy()
     rows = bf16_bits_to_f32(b.rows).copy()
     q[:] = 0.0
