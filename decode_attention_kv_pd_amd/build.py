@@ -7,6 +7,7 @@ binding loads it from.
 """
 from __future__ import annotations
 
+import importlib.util
 import os
 import shutil
 import subprocess
@@ -80,6 +81,13 @@ def build(verbose: bool = False) -> str:
         if res.returncode != 0:
             raise RuntimeError(f"link failed ({res.returncode}):\n{_errors(res)}")
     os.replace(tmp, LIB)
+    # static checks of the 32-row MLA kernel's generated code (isa_check.py)
+    spec = importlib.util.spec_from_file_location("_pd_isa_check", os.path.join(HERE, "isa_check.py"))
+    chk = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(chk)
+    chk.run(hipcc(), COMMON)
+    if verbose:
+        print("isa check: mla_wide_kernel ok", flush=True)
     return LIB
 
 
