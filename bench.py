@@ -63,8 +63,8 @@ def parse():
                     help="skip the interference / chunked-prefill sweep")
     ap.add_argument("--sweep-decodes", type=int, default=32, help="decodes in the 1PnD sweep batches")
     ap.add_argument("--no-mla", action="store_true", help="skip the latent-cache (MLA) decode legs")
-    ap.add_argument("--cpu-decode-requests", type=int, default=24)
-    ap.add_argument("--cpu-prefill-tokens", type=int, default=16)
+    ap.add_argument("--cpu-decode-requests", type=int, default=60)
+    ap.add_argument("--cpu-prefill-tokens", type=int, default=40)
     return ap.parse_args()
 
 
