@@ -150,3 +150,18 @@ def test_pack_unpack_reject_bad_lists_before_device_work():
         expect("PD_ERR_WORKSPACE", fn, d, pool, 10, [1, 2, 3], FakeTensor(3 * pb), scr, stream=0)
         expect("PD_ERR_WORKSPACE", fn, d, pool, 10, [1, 2], FakeTensor(pb), scr, stream=0)
         expect("PD_ERR_UNSUPPORTED", fn, mdesc(kv_lora_rank=128), pool, 10, [1], buf, scr, stream=0)
+
+
+def test_chunk_length_fills_one_dispatch_round():
+    """At 64 requests x U{1024..8192} keys the planner's chunk length gives
+    at most one block per CU (one dispatch round) while still splitting the
+    long requests; asking for fewer CUs gives longer chunks."""
+    for wid in ("mla_tp8", "mla_dp"):
+        b = make_mla_batch(wid, materialize=False)
+        p = plan_of(b)
+        s = p.stats()
+        assert 128 < s.decode_units <= 256
+        assert s.decode_chunk_keys < int(b.kv_lens.max())
+        q = plan_of(b, num_cus=64)
+        assert q.stats().decode_chunk_keys > s.decode_chunk_keys
+        check_cover(b, q)
