@@ -118,6 +118,7 @@ RAGGED = [
     dict(lengths=([2, 1, 0, 1], [90, 40, 7, 1]), heads=16, causal=False),
     dict(lengths=([3, 1], [40, 1]), heads=128, causal=False),
     dict(lengths=([4, 2, 1], [4, 70, 33]), heads=128, page_size=16),
+    dict(lengths=([1, 1, 3], [40000, 129, 2500]), heads=128, page_size=128),   # long cache, big pages
 ]
 
 
