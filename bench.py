@@ -395,7 +395,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU sharding in this build).", file=sys.stderr)
+              "(no multi-GPU sharding is implemented).", file=sys.stderr)
         sys.exit(2)
     import torch
 
