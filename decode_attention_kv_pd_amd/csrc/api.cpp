@@ -179,6 +179,27 @@ pd_status staged_upload(void* dst, const void* src, size_t n, hipStream_t stream
 
 namespace {
 
+int64_t round_up32(int64_t x) { return (x + 31) / 32 * 32; }
+
+constexpr int64_t kMaxParts = (int64_t)1 << 26;  // split-KV partial results of one plan
+
+// A caller's decode_chunk_keys (> 0), rounded up to a multiple of 32 and
+// clamped to the longest request (rounded up), so that no length arithmetic
+// can overflow and a chunk is never longer than the keys it could cover.
+int clamp_chunk_option(int32_t keys, const pd_plan_s& P) {
+  int64_t max_kv = 32;
+  for (const pdk::ReqInfo& ri : P.req) max_kv = std::max<int64_t>(max_kv, ri.kv);
+  const int64_t c = std::min({round_up32(keys), round_up32(max_kv), (int64_t)1 << 30});
+  return (int)std::max<int64_t>(c, 32);
+}
+
+// Length of each of the equal chunks (a multiple of 32 keys) that kv >= 1
+// keys split into at a chunk length of about `chunk` (> 0).
+int equal_chunk_len(int32_t kv, int chunk) {
+  const int64_t nch = ((int64_t)kv + chunk - 1) / chunk;
+  return (int)std::min<int64_t>(round_up32(((int64_t)kv + nch - 1) / nch), (int64_t)1 << 30);
+}
+
 pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   const pd_attn_desc& d = P.desc;
   const int g = P.g;
@@ -257,7 +278,7 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   }
   int chunk = 0;
   if (opts && opts->decode_chunk_keys > 0) {
-    chunk = (opts->decode_chunk_keys + 31) / 32 * 32;
+    chunk = clamp_chunk_option(opts->decode_chunk_keys, P);
   } else if (decode_keys > 0) {
     const int64_t target_units = (int64_t)num_cus * 16;
     int64_t c = (decode_keys + target_units - 1) / target_units;
@@ -269,18 +290,20 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   for (int r = 0; r < P.B; ++r) {
     const pdk::ReqInfo& ri = P.req[r];
     if (ri.qo == 0 || (int64_t)ri.qo * g > pdk::kDecodeCols) continue;
-    int nch = (ri.kv + chunk - 1) / chunk;
-    int len = (ri.kv + nch - 1) / nch;
-    len = (len + 31) / 32 * 32;
-    nch = (ri.kv + len - 1) / len;
+    const int len = equal_chunk_len(ri.kv, chunk);
+    const int nch = (int)(((int64_t)ri.kv + len - 1) / len);
+    if ((int64_t)P.n_parts + (int64_t)nch * H_kv > kMaxParts)
+      return fail(PD_ERR_UNSUPPORTED, "more than 2^26 split-KV decode units");
     for (int hk = 0; hk < H_kv; ++hk) {
       P.mg.push_back({r, hk, P.n_parts, nch});
       for (int c = 0; c < nch; ++c) {
-        const int k0 = c * len, k1 = std::min(ri.kv, k0 + len);
+        const int k0 = (int)((int64_t)c * len), k1 = (int)std::min<int64_t>(ri.kv, (int64_t)k0 + len);
         units.push_back({r, hk, k0, k1, P.n_parts++, 0, 0, 0});
       }
     }
   }
+  for (const pdk::MergeGroup& m : P.mg)
+    if (m.nparts < 1) return fail(PD_ERR_INVALID_ARG, "planner: a decode row group without a key chunk");
   std::stable_sort(units.begin(), units.end(), [](const pdk::DecodeItem& a, const pdk::DecodeItem& b) {
     return (a.k1 - a.k0) > (b.k1 - b.k0);
   });
@@ -444,12 +467,6 @@ pdk::AttnParams attn_params(const pd_plan_s& P, void* d_ws) {
 // multiple of 32 keys) so that about two blocks per CU exist; the blocks of
 // one (request, chunk) read the same cache rows and are placed on one XCD,
 // one dispatch round apart (block i runs on XCD i % 8), longest first.
-// Keys of the chunks a request of kv keys splits into at a chunk length of
-// about `chunk`: equal lengths, multiples of 32.
-int mla_chunk_len(int kv, int chunk) {
-  const int nch = (kv + chunk - 1) / chunk;
-  return ((kv + nch - 1) / nch + 31) / 32 * 32;
-}
 
 // Chunk length for an MLA plan. A block stages the whole latent row once per
 // 32-key step for all its query rows, holds one CU (its LDS ring takes most of
@@ -465,7 +482,7 @@ int mla_pick_chunk(const pd_plan_s& P, int R, int num_cus) {
   int max_kv = 0;
   for (int r = 0; r < P.B; ++r)
     if (P.req[r].qo > 0) max_kv = std::max(max_kv, P.req[r].kv);
-  const int top = std::max(256, std::min(16384, (max_kv + 127) / 128 * 128));
+  const int top = (int)std::max<int64_t>(256, std::min<int64_t>(16384, ((int64_t)max_kv + 127) / 128 * 128));
   std::vector<int> cand;
   for (double c = 256; c < top * 1.2; c *= 1.125) {
     const int v = std::min(top, ((int)c + 127) / 128 * 128);
@@ -481,11 +498,12 @@ int mla_pick_chunk(const pd_plan_s& P, int R, int num_cus) {
       const pdk::ReqInfo& ri = P.req[r];
       if (ri.qo == 0) continue;
       const int ng = (int)(((int64_t)ri.qo * P.mdesc.num_qo_heads + R - 1) / R);
-      const int len = mla_chunk_len(ri.kv, chunk);
-      const int nch = (ri.kv + len - 1) / len;
+      const int len = equal_chunk_len(ri.kv, chunk);
+      const int nch = (int)(((int64_t)ri.kv + len - 1) / len);
       if (nch > 1) parts += (int64_t)ng * nch;
       for (int c = 0; c < nch; ++c)
-        for (int g = 0; g < ng; ++g) blk.push_back(std::min(ri.kv, (c + 1) * len) - c * len);
+        for (int g = 0; g < ng; ++g)
+          blk.push_back((int)(std::min<int64_t>(ri.kv, (int64_t)(c + 1) * len) - (int64_t)c * len));
     }
     if (blk.size() > (size_t)64 * num_cus && chunk != top) continue;  // far past one CU each
     std::sort(blk.begin(), blk.end(), std::greater<int>());
@@ -522,7 +540,7 @@ pd_status build_mla_plan(pd_plan_s& P, const pd_plan_options* opts) {
   }
   int chunk = 0;
   if (opts && opts->decode_chunk_keys > 0) {
-    chunk = (opts->decode_chunk_keys + 31) / 32 * 32;
+    chunk = clamp_chunk_option(opts->decode_chunk_keys, P);
   } else if (work > 0) {
     chunk = mla_pick_chunk(P, R, num_cus);
   }
@@ -536,15 +554,18 @@ pd_status build_mla_plan(pd_plan_s& P, const pd_plan_options* opts) {
     const pdk::ReqInfo& ri = P.req[r];
     if (ri.qo == 0) continue;
     const int ng = (int)(((int64_t)ri.qo * H + R - 1) / R);
-    const int len = mla_chunk_len(ri.kv, chunk);
-    const int nch = (ri.kv + len - 1) / len;
+    const int len = equal_chunk_len(ri.kv, chunk);
+    const int nch = (int)(((int64_t)ri.kv + len - 1) / len);
     nchunks[r] = nch;
+    if (nch < 1 || (int64_t)P.n_parts + (int64_t)ng * nch > kMaxParts)
+      return fail(PD_ERR_UNSUPPORTED, "MLA plan: more than 2^26 partial results");
     if (nch > 1) {  // slots [base, base + ng * nch): row group rg's chunk c at base + rg * nch + c
       base[r] = P.n_parts;
       for (int rg = 0; rg < ng; ++rg) P.mmg.push_back({r, rg, P.n_parts + rg * nch, nch});
       P.n_parts += ng * nch;
     }
-    for (int c = 0; c < nch; ++c) tasks.push_back({r, c, c * len, std::min(ri.kv, (c + 1) * len), ng});
+    for (int c = 0; c < nch; ++c)
+      tasks.push_back({r, c, (int)((int64_t)c * len), (int)std::min<int64_t>(ri.kv, (int64_t)(c + 1) * len), ng});
   }
   std::stable_sort(tasks.begin(), tasks.end(),
                    [](const Task& a, const Task& b) { return (a.k1 - a.k0) > (b.k1 - b.k0); });

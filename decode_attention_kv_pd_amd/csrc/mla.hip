@@ -3,7 +3,7 @@
 // its partial results, and the append of new latent rows.
 //
 // What is computed (Perplexity post "Disaggregated prefill and decode",
-// section "Sharded KV Cache Transfers", DeepSeek paragraphs): MLA keeps one
+// section "DeepSeek-R1" under "Disaggregated Deployments"): MLA keeps one
 // latent vector per token for all KV heads, the same on every rank.  Decode
 // uses the absorbed form: each query row (token t, head h) brings a
 // [latent ; rotary] vector q, and

@@ -1,7 +1,7 @@
 // MLA decode with 32 query rows per wavefront (32x32x16 bf16 products), for
 // requests whose tokens bring 128 query heads.  What is computed is the same
 // as in mla.hip (Perplexity post "Disaggregated prefill and decode", section
-// "Sharded KV Cache Transfers", DeepSeek paragraphs: absorbed-form attention
+// "DeepSeek-R1" under "Disaggregated Deployments": absorbed-form attention
 // with one latent KV head, key = the whole 576-entry cache row, value = its
 // first 512 entries).
 //

@@ -397,8 +397,8 @@ pd_status pd_kv_unpack_layers(pd_xfer_t xfer, void* d_ws, const void* d_buf,
 void pd_xfer_free(pd_xfer_t xfer);
 
 /* ---- MLA decode over a latent KV cache --------------------------------
- * Perplexity, "Disaggregated prefill and decode", section "Sharded KV Cache
- * Transfers" (DeepSeek paragraphs): multi-head latent attention compresses
+ * Perplexity, "Disaggregated prefill and decode", section "DeepSeek-R1"
+ * (under "Disaggregated Deployments"): multi-head latent attention compresses
  * every KV head of a token into one latent vector, so tensor parallelism
  * cannot split the cache by heads.  Every rank holds the same latent cache,
  * and the heads are only separated after decompression.  The pages give no

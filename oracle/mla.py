@@ -3,7 +3,7 @@ latent KV cache -- test infrastructure.  Only ``tests/``, the smoke check and
 the benchmark's CPU baseline import it; the HIP path shares no code with it.
 
 What the pages fix (Perplexity, "Disaggregated prefill and decode", section
-"Sharded KV Cache Transfers", the DeepSeek paragraphs): DeepSeek's MLA
+"DeepSeek-R1" under "Disaggregated Deployments"): DeepSeek's MLA
 compresses all KV heads of a token into a single latent vector, so tensor
 parallelism cannot split the cache by heads.  Every rank holds the same
 latent cache, and the heads are only separated after decompression.  The

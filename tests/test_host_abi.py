@@ -306,3 +306,20 @@ def test_block_map_covers_work_and_keeps_xcd_affinity(order):
         assert first_d < len(pf)
     else:            # prefill tiles first
         assert (bmap[:len(pf)] >= 0).all()
+
+
+@pytest.mark.parametrize("chunk", [2_147_483_647, 2_147_483_000, 2_147_483_616, 1 << 30, 40, 31])
+def test_decode_chunk_option_near_int32_max_still_covers_every_row(chunk):
+    """A decode_chunk_keys option near INT32_MAX is clamped, not wrapped: the
+    plan still gives every decode row group at least one key chunk and the
+    chunks tile [0, kv) exactly (no merge group without partial results)."""
+    b = make_batch("mixed", materialize=False,
+                   lengths=([1, 1, 4, 1, 300], [4096, 33, 1500, 1, 300]))
+    d = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype, b.causal)
+    plan = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages,
+                      decode_chunk_keys=chunk)
+    check_cover(b, plan)
+    mg = plan.work_items(2)
+    assert (mg[:, 3] >= 1).all()
+    s = plan.stats()
+    assert 32 <= s.decode_chunk_keys <= 4096 + 31

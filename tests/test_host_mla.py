@@ -165,3 +165,13 @@ def test_chunk_length_fills_one_dispatch_round():
         q = plan_of(b, num_cus=64)
         assert q.stats().decode_chunk_keys > s.decode_chunk_keys
         check_cover(b, q)
+
+
+@pytest.mark.parametrize("chunk", [2_147_483_647, 2_147_483_000, 1 << 30, 33])
+def test_decode_chunk_option_near_int32_max_still_covers_every_row(chunk):
+    """The latent planner clamps a huge decode_chunk_keys instead of wrapping
+    it: every (request, row group) still has blocks covering [0, kv)."""
+    for wid, kw in (("mla_tiny", {}), ("mla_tiny", dict(lengths=([2, 1], [2000, 33]), heads=128,
+                                                         page_size=128))):
+        b = make_mla_batch(wid, materialize=False, **kw)
+        check_cover(b, plan_of(b, decode_chunk_keys=chunk))

@@ -262,8 +262,8 @@ def device_seed(wid: int, rep: int, stream: int) -> int:
 
 
 # ------------------------------------------------------------ MLA workloads
-# Latent KV cache (multi-head latent attention, post section "Sharded KV Cache
-# Transfers", DeepSeek paragraphs): one row of d_c + d_r values per token,
+# Latent KV cache (multi-head latent attention, post section "DeepSeek-R1"
+# under "Disaggregated Deployments"): one row of d_c + d_r values per token,
 # shared by every query head.  Dimensions are DeepSeek-V3's published
 # configuration (latent 512, rotary key 64, 128 query heads, softmax scale
 # 1 / sqrt(128 + 64)); the pages give none.
