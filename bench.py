@@ -13,17 +13,28 @@ page size 64; pool of 138164 pages = 36.2 GB, drawn on the device):
   pd_kv_pack / pd_kv_unpack  the chunk request's 512 pages (128 MiB) into a
                              transfer buffer and back into other pages
 
-It is the one workload whose step exercises every part of the path; the
-other workloads are parity cases of the test suite.  Inputs are resident in
-HBM before the timed region.  W warm-up steps, then K timed steps between
-device synchronisations; per-phase times come from HIP events recorded on the
-launch stream.  Afterwards, untimed legs run decode-only and prefill-only
-plans over the same pool (per-phase GB/s and TFLOP/s, interference ratio),
-and the CPU oracle is timed on a bounded sample of the same workload.
+It is the one workload whose step exercises every part of the path.  Inputs
+are resident in HBM before the timed region.  W warm-up steps, then K timed
+steps between device synchronisations; per-phase times come from HIP events
+recorded on the launch stream (torch's current stream, which the binding
+launches on).  Each step streams the 34 GB decode cache, which evicts the L2
+and the MALL by itself.
+
+Afterwards, untimed legs measure:
+  * decode-only and prefill-only plans over the same pool (per-phase GB/s and
+    TFLOP/s, interference ratio);
+  * the decode (64 x kv U{512..4096}, 40/40 heads), prefill (8 x 512 causal,
+    40/40 heads) and mixed (one 1024-token prefill + 63 decodes, 32/8 heads)
+    workloads;
+  * transfers, the interference sweep and the latent-cache decode;
+  * the CPU oracle on a bounded sample, over a process pool.
+Every leg times one call per repetition with HIP events after streaming a
+1 GiB buffer (so L2 and MALL start cold), and reports median, min and p90;
+calls shorter than 50 us are also timed as 100 back-to-back launches.
 
 Prints one JSON line.  ``value`` is the step's attainment of the MI355X
 roofline in percent: the ideal time of the step's algorithmic work at peak
-(attention launch: max of its HBM bytes / 8 TB/s and its prefill flops /
+(attention launch: max of its decode bytes / 8 TB/s and its prefill flops /
 2.5 PFLOP/s; append, pack, unpack: bytes / 8 TB/s) divided by the measured
 time per step.
 """
@@ -31,7 +42,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -45,45 +55,49 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E, 8 TB/s
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 METRIC = "decode attn HBM GB/s + prefill attn TFLOP/s (% of MI355X peak), 1 GPU"
+SHORT_MS = 0.05              # calls shorter than this are also timed back to back
+B2B_LAUNCHES = 100
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long")
-    ap.add_argument("--phase-reps", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=20, help="timed repetitions of each leg")
+    ap.add_argument("--leg-warmup", type=int, default=5, help="untimed calls before each leg")
     ap.add_argument("--no-phases", action="store_true", help="skip the decode-only / prefill-only legs")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the decode / prefill / mixed workload legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-transfers", action="store_true",
-                    help="skip the head-range and multi-layer transfer legs")
+                    help="skip the pack / unpack, head-range and multi-layer transfer legs")
     ap.add_argument("--layers", type=int, default=8, help="layers of the multi-layer pack leg")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the interference / chunked-prefill sweep")
     ap.add_argument("--sweep-decodes", type=int, default=32, help="decodes in the 1PnD sweep batches")
     ap.add_argument("--no-mla", action="store_true", help="skip the latent-cache (MLA) decode legs")
-    ap.add_argument("--cpu-decode-requests", type=int, default=60)
-    ap.add_argument("--cpu-prefill-tokens", type=int, default=40)
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle processes (0: the host's available cores, at most 16)")
+    ap.add_argument("--cpu-decode-rows", type=int, default=8, help="decode rows per oracle process")
+    ap.add_argument("--cpu-prefill-rows", type=int, default=6, help="prefill-chunk rows per oracle process")
     return ap.parse_args()
 
 
 def algorithmic_work(b, elt=2):
-    """Bytes and flops the method must move / compute (not the dense work
-    it avoids): decode rows read their K/V once plus Q, write O (fp32) and
-    LSE; prefill flops count visible (query, key) pairs only (4 D flops per
-    pair per query head); the prefill request's compulsory bytes are its
-    Q, K/V and O.  Append reads and writes each new row; pack / unpack read
-    and write each page."""
-    g = b.H_q // b.H_kv
-    dec_bytes = pre_bytes = 0
-    flops = 0
+    """What the method must move or compute, not the dense work it avoids.
+    Decode requests (qo = 1) read their K/V once, read Q and write O (fp32):
+    decode bytes.  Prefill requests (qo > 1) do 4 D flops per visible
+    (query, key) pair per query head: prefill flops; their compulsory bytes
+    are Q, K/V and O.  Append reads and writes each new row."""
+    dec_bytes = pre_bytes = flops = 0
     for qo, kv in zip(b.qo_lens.tolist(), b.kv_lens.tolist()):
         if qo == 0:
             continue
         kvb = 2 * kv * b.H_kv * b.D * elt
-        qob = qo * b.H_q * (b.D * elt + b.D * 4 + 4)
-        if qo * g <= 16:
+        qob = qo * b.H_q * b.D * (elt + 4)
+        if qo == 1:
             dec_bytes += kvb + qob
         else:
             pre_bytes += kvb + qob
@@ -114,84 +128,285 @@ def measured_traffic(workload):
     return None
 
 
-def cpu_baseline(b, n_dec, n_tok):
-    """Time the float64 oracle on a bounded sample of the workload: n_dec
-    decode requests (all heads, full 32768-token cache) and n_tok tokens of
-    the prefill chunk (all heads).  Inputs are drawn on the host with the
-    workload's distribution; only the oracle call is timed, with BLAS held to
-    one thread."""
-    from threadpoolctl import threadpool_limits
-
-    from oracle import attention as OA
-    from workloads import f32_to_bf16_bits, bf16_bits_to_f32
-
-    rng = np.random.default_rng(np.random.SeedSequence([2026, b.wid, 99]))
-    g = b.H_q // b.H_kv
-
-    def draw(*shape):
-        return bf16_bits_to_f32(f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))).astype(np.float64)
-
-    secs = 0.0
-    dec_bytes = pre_flops = 0
-    kv = int(b.kv_lens[0])
-    k, v = draw(kv, b.H_kv, b.D), draw(kv, b.H_kv, b.D)   # one cache, reused by every sampled request
-    with threadpool_limits(limits=1):
-        for i in range(n_dec + 1):
-            if i < n_dec:     # a decode request: one row, all heads
-                q = draw(1, b.H_q, b.D)
-                pos = np.array([kv - 1])
-                dec_bytes += 2 * kv * b.H_kv * b.D * 2 + b.H_q * (b.D * 2 + b.D * 4 + 4)
-            else:             # prefill tokens spread over the chunk
-                qo = int(b.qo_lens[0])
-                toks = np.linspace(0, qo - 1, n_tok).astype(np.int64)
-                q = draw(n_tok, b.H_q, b.D)
-                pos = kv - qo + toks
-                pre_flops += int(4 * b.D * b.H_q * (pos + 1).sum())
-            t0 = time.perf_counter()
-            OA.attend(q, k, v, pos, b.sm_scale, True)
-            secs += time.perf_counter() - t0
-    ideal = dec_bytes / (PEAK_HBM_GBPS * 1e9) + pre_flops / (PEAK_BF16_TFLOPS * 1e12)
-    return {"value": 100.0 * ideal / secs, "unit": "% of MI355X peak", "cores": 1, "kind": "oracle",
-            "sample": f"{n_dec} decode rows x {b.H_q} heads over {kv} keys + {n_tok} prefill-chunk "
-                      f"rows x {b.H_q} heads (float64 numpy oracle, 1 BLAS thread; one drawn cache "
-                      f"shared by the sampled rows)",
-            "seconds": round(secs, 3), "decode_GBps": dec_bytes / secs / 1e9 if n_dec else None,
-            "prefill_TFLOPs": pre_flops / secs / 1e12 if n_tok else None}
+def spread(ts):
+    ts = np.asarray(ts, np.float64)
+    return {"median": round(float(np.median(ts)), 4), "min": round(float(ts.min()), 4),
+            "p90": round(float(np.percentile(ts, 90)), 4), "mean": round(float(ts.mean()), 4),
+            "reps": int(ts.size)}
 
 
-def transfer_legs(args, pd, torch, b, desc, pool, pack_ids, unpack_ids):
-    """Head-range pack / unpack of the chunk request's pages (half of the KV
-    heads: what a rank sends when the decoder has twice the prefiller's TP
-    degree), and a multi-layer pack of the same page count over `--layers`
-    layer pools in one launch, with per-layer progress counters in pinned
-    host memory polled from the host.  Bytes are read + written."""
-    from workloads import device_normal_, device_seed
+class Meter:
+    """Times device calls with HIP events on torch's current stream, which is
+    the stream the binding launches on."""
 
-    def timed(fn, reps):
+    def __init__(self, torch, reps, warmup, flush_bytes=1 << 30):
+        self.torch = torch
+        self.reps = reps
+        self.warmup = warmup
+        self.flush_buf = torch.zeros(flush_bytes // 4, dtype=torch.int32, device="cuda")
+
+    def flush(self):
+        # reads and writes 1 GiB: evicts the L2 of every XCD and the MALL
+        self.flush_buf.add_(1)
+
+    def time(self, fn, flush=True, b2b=None):
+        torch = self.torch
+        for _ in range(self.warmup):
+            fn()
+        torch.cuda.synchronize()
         ts = []
-        for _ in range(reps):
+        for _ in range(self.reps):
+            if flush:
+                self.flush()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             fn()
             e1.record()
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
-        return float(np.median(ts))
+        r = spread(ts)
+        r["flushed"] = bool(flush)
+        if b2b or (b2b is None and r["median"] < SHORT_MS):
+            if flush:
+                self.flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(B2B_LAUNCHES):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            r["b2b100_ms"] = round(e0.elapsed_time(e1) / B2B_LAUNCHES, 4)
+        return r
+
+
+# ------------------------------------------------------------------ CPU oracle
+def _cpu_worker(idx, barrier, out_q, spec):
+    """One oracle process: draws its share of the sample (the workload's
+    distribution), waits for every process, then times its oracle calls."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as OA
+    from workloads import bf16_bits_to_f32, f32_to_bf16_bits
+
+    rng = np.random.default_rng(np.random.SeedSequence([2026, spec["wid"], 99, idx]))
+
+    def draw(*shape):
+        return bf16_bits_to_f32(f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))).astype(np.float64)
+
+    kv, qo, H_q, H_kv, D = spec["kv"], spec["qo"], spec["H_q"], spec["H_kv"], spec["D"]
+    k, v = draw(kv, H_kv, D), draw(kv, H_kv, D)           # one cache, shared by this process's rows
+    qd = draw(spec["n_dec"], H_q, D)
+    toks = rng.integers(0, qo, size=spec["n_pre"])         # prefill-chunk rows at random positions
+    qp = draw(spec["n_pre"], H_q, D)
+    with threadpool_limits(limits=1):
+        barrier.wait(timeout=300)
+        t0 = time.perf_counter()
+        for i in range(spec["n_dec"]):
+            OA.attend(qd[i:i + 1], k, v, np.array([kv - 1]), spec["scale"], True)
+        t1 = time.perf_counter()
+        for i in range(spec["n_pre"]):
+            OA.attend(qp[i:i + 1], k, v, np.array([kv - qo + int(toks[i])]), spec["scale"], True)
+        t2 = time.perf_counter()
+    dec_bytes = spec["n_dec"] * (2 * kv * H_kv * D * 2 + H_q * D * 6)
+    flops = int(sum(4 * D * H_q * (kv - qo + int(t) + 1) for t in toks))
+    out_q.put((idx, t0, t1, t2, dec_bytes, flops))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(b, workers, n_dec, n_pre):
+    """The float64 oracle timed on the host's cores: `workers` processes
+    (one BLAS thread each), each computing n_dec decode rows (64 heads over a
+    32768-token cache) and n_pre rows of the 8192-token chunk (64 heads, over
+    its causal key range).  Throughput = the sample's work over the wall time
+    from the moment every process has its inputs drawn to the moment the last
+    one finishes, in the step's unit."""
+    import multiprocessing as mp
+
+    if workers <= 0:
+        try:
+            avail = len(os.sched_getaffinity(0))
+        except AttributeError:
+            avail = os.cpu_count() or 1
+        workers = max(1, min(avail, 16))
+    spec = {"wid": b.wid, "kv": int(b.kv_lens[0]), "qo": int(b.qo_lens[0]), "H_q": b.H_q, "H_kv": b.H_kv,
+            "D": b.D, "scale": b.sm_scale, "n_dec": n_dec, "n_pre": n_pre}
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(workers)
+    q = ctx.Queue()
+    procs = [ctx.Process(target=_cpu_worker, args=(i, barrier, q, spec)) for i in range(workers)]
+    for p in procs:
+        p.start()
+    res = [q.get(timeout=900) for _ in procs]
+    for p in procs:
+        p.join()
+    t_start = min(r[1] for r in res)
+    t_dec_end = max(r[2] for r in res)
+    t_end = max(r[3] for r in res)
+    dec_bytes = sum(r[4] for r in res)
+    flops = sum(r[5] for r in res)
+    secs = t_end - t_start
+    ideal = dec_bytes / (PEAK_HBM_GBPS * 1e9) + flops / (PEAK_BF16_TFLOPS * 1e12)
+    busy = sum(r[3] - r[1] for r in res)
+    return {"value": 100.0 * ideal / secs, "unit": "% of MI355X peak", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{workers} processes x ({n_dec} decode rows x {b.H_q} heads over {spec['kv']} keys + "
+                      f"{n_pre} chunk rows x {b.H_q} heads at random chunk positions); float64 numpy "
+                      f"oracle, one BLAS thread per process, each process with its own drawn cache",
+            "seconds": round(secs, 3), "cpu_seconds": round(busy, 3),
+            "decode_GBps": round(dec_bytes / max(t_dec_end - t_start, 1e-9) / 1e9, 4),
+            "prefill_TFLOPs": round(flops / max(t_end - t_dec_end, 1e-9) / 1e12, 6)}
+
+
+# ------------------------------------------------------------------- helpers
+def device_inputs(torch, b, pd, salt=0):
+    """Pool, Q, new K/V, outputs of a workload, drawn on the device."""
+    from workloads import device_normal_, device_seed
+    n = max(int(b.qo_lens.sum()), 1)
+    t = {"pool": device_normal_(torch.empty(b.pool_shape, dtype=torch.bfloat16, device="cuda"),
+                                device_seed(b.wid, salt, 0)),
+         "q": device_normal_(torch.empty((n, b.H_q, b.D), dtype=torch.bfloat16, device="cuda"),
+                             device_seed(b.wid, salt, 1)),
+         "k_new": device_normal_(torch.empty((n, b.H_kv, b.D), dtype=torch.bfloat16, device="cuda"),
+                                 device_seed(b.wid, salt, 2)),
+         "v_new": device_normal_(torch.empty((n, b.H_kv, b.D), dtype=torch.bfloat16, device="cuda"),
+                                 device_seed(b.wid, salt, 3)),
+         "out": torch.empty((n, b.H_q, b.D), dtype=torch.float32, device="cuda"),
+         "lse": torch.empty((n, b.H_q), dtype=torch.float32, device="cuda")}
+    return t
+
+
+def sub_plan(pd, torch, b, desc, sel, q, **kw):
+    """Plan, workspace, Q rows and outputs for the requests selected by `sel`
+    (the others get qo = 0), over the same pool."""
+    qo = np.where(sel, b.qo_lens, 0).astype(np.int32)
+    p = pd.pd_plan(desc, qo, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages, **kw)
+    ws = torch.empty(max(p.workspace_bytes, 1), dtype=torch.uint8, device="cuda")
+    pd.pd_plan_upload(p, ws)
+    idx = np.concatenate([np.arange(b.qo_indptr[r], b.qo_indptr[r + 1]) for r in range(b.B) if sel[r]])
+    qs = q[torch.as_tensor(idx, device="cuda")].contiguous()
+    o = torch.empty((len(idx), b.H_q, b.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((len(idx), b.H_q), dtype=torch.float32, device="cuda")
+    return p, ws, qs, o, lse
+
+
+def roofline_entry(w, t_ms):
+    """Per-phase figures of one attention call of t_ms against MI355X peaks."""
+    hbm_ms = w["decode_bytes"] / (PEAK_HBM_GBPS * 1e9) * 1e3
+    mfma_ms = w["prefill_flops"] / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+    return {"decode_GBps": round(w["decode_bytes"] / (t_ms * 1e-3) / 1e9, 1),
+            "prefill_TFLOPs": round(w["prefill_flops"] / (t_ms * 1e-3) / 1e12, 1),
+            "roofline_frac_strict": round(max(hbm_ms, mfma_ms) / t_ms, 4),
+            "roofline_frac_sum": round((hbm_ms + mfma_ms) / t_ms, 4)}
+
+
+# --------------------------------------------------- decode / prefill / mixed
+def config_legs(args, pd, torch, meter):
+    """The decode, prefill and mixed workloads, each on its own pool: append
+    and attention timed per call (flushed caches), with per-phase rates, the
+    prefill workload's attainable rate (its compulsory Q, K/V and O bytes
+    make it HBM-bound when the caches are cold) and, for the mixed workload,
+    decode-only and prefill-only plans and the interference ratio."""
+    from workloads import make_batch
+
+    res = {}
+    for wid in ("decode", "prefill", "mixed"):
+        b = make_batch(wid, materialize=False)
+        desc = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype, b.causal, b.sm_scale)
+        t = device_inputs(torch, b, pd)
+        w = algorithmic_work(b)
+        h0 = time.perf_counter()
+        plan = pd.pd_plan(desc, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages)
+        plan_ms = (time.perf_counter() - h0) * 1e3
+        ws = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device="cuda")
+        pd.pd_plan_upload(plan, ws)
+        app = meter.time(lambda: pd.pd_kv_append(plan, ws, t["pool"], t["k_new"], t["v_new"]))
+        att = meter.time(lambda: pd.pd_attention_run(plan, ws, t["q"], t["pool"], t["out"], t["lse"]))
+        assert torch.isfinite(t["out"]).all().item(), f"{wid}: non-finite attention output"
+        st = plan.stats()
+        e = {"shape": f"B {b.B}, H {b.H_q}/{b.H_kv}, D {b.D}, page {b.ps}, bf16",
+             "plan_host_ms": round(plan_ms, 4),
+             "plan": {"prefill_tiles": st.prefill_tiles, "decode_units": st.decode_units,
+                      "decode_chunk_keys": st.decode_chunk_keys},
+             "append_ms": app, "append_GBps": round(w["append_bytes"] / (app["median"] * 1e-3) / 1e9, 1),
+             "attention_ms": att}
+        tm = att["median"]
+        if wid == "decode":
+            gbps = w["decode_bytes"] / (tm * 1e-3) / 1e9
+            e.update({"decode_bytes": w["decode_bytes"], "GBps": round(gbps, 1),
+                      "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4), "target_ms_at_70pct":
+                      round(w["decode_bytes"] / (0.7 * PEAK_HBM_GBPS * 1e9) * 1e3, 4)})
+        elif wid == "prefill":
+            tf = w["prefill_flops"] / (tm * 1e-3) / 1e12
+            t_mfma = w["prefill_flops"] / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+            t_hbm = w["prefill_bytes"] / (PEAK_HBM_GBPS * 1e9) * 1e3
+            t_att = max(t_mfma, t_hbm)
+            e.update({"prefill_flops": w["prefill_flops"], "compulsory_bytes": w["prefill_bytes"],
+                      "TFLOPs": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "attainable_ms": round(t_att, 4), "frac_of_attainable": round(t_att / tm, 4)})
+            if "b2b100_ms" in att:
+                e["frac_of_attainable_b2b"] = round(t_att / att["b2b100_ms"], 4)
+        else:
+            e.update({"decode_bytes": w["decode_bytes"], "prefill_flops": w["prefill_flops"]})
+            e.update(roofline_entry(w, tm))
+            dec = b.qo_lens == 1
+            for name, sel in (("decode_only", dec), ("prefill_only", ~dec)):
+                p, wsp, qs, o, lse = sub_plan(pd, torch, b, desc, sel, t["q"])
+                r = meter.time(lambda: pd.pd_attention_run(p, wsp, qs, t["pool"], o, lse))
+                if name == "decode_only":
+                    r["GBps"] = round(w["decode_bytes"] / (r["median"] * 1e-3) / 1e9, 1)
+                    r["frac_of_peak"] = round(r["GBps"] / PEAK_HBM_GBPS, 4)
+                else:
+                    r["TFLOPs"] = round(w["prefill_flops"] / (r["median"] * 1e-3) / 1e12, 1)
+                    r["frac_of_peak"] = round(r["TFLOPs"] / PEAK_BF16_TFLOPS, 4)
+                e[name] = r
+                p.close()
+            e["interference_ratio"] = round(tm / e["decode_only"]["median"], 3)
+            e["mixed_vs_sum"] = round(tm / (e["decode_only"]["median"] + e["prefill_only"]["median"]), 3)
+        res[wid] = e
+        plan.close()
+        del t, ws
+        torch.cuda.synchronize()
+        print(f"[bench] {wid} workload leg done", file=sys.stderr, flush=True)
+    return res
+
+
+# ------------------------------------------------------------------ transfers
+def transfer_legs(args, pd, torch, meter, b, desc, pool, pack_ids, unpack_ids):
+    """Pack / unpack of the chunk request's pages (whole pages, then half of
+    the KV heads: what a rank sends when the decoder has twice the
+    prefiller's TP degree), timed per call after a cache flush, and a
+    multi-layer pack of the same page count over `--layers` layer pools in
+    one launch, with per-layer progress counters in pinned host memory
+    polled from the host.  Bytes are read + written."""
+    from workloads import device_normal_, device_seed
 
     out = {}
     n = len(pack_ids)
+    nb = pd.pd_kv_pack_bytes(desc, n)
+    buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    scr = torch.empty(4 * n, dtype=torch.uint8, device="cuda")
+    r = meter.time(lambda: pd.pd_kv_pack(desc, pool, b.num_pool_pages, pack_ids, buf, scr))
+    out["pack"] = {"pages": n, "bytes": nb, "ms": r, "GBps": round(2 * nb / (r["median"] * 1e-3) / 1e9, 1)}
+    r = meter.time(lambda: pd.pd_kv_unpack(desc, pool, b.num_pool_pages, unpack_ids, buf, scr))
+    out["unpack"] = {"ms": r, "GBps": round(2 * nb / (r["median"] * 1e-3) / 1e9, 1)}
+    del buf
     h1 = b.H_kv // 2
     nb = pd.pd_kv_pack_heads_bytes(desc, n, 0, h1)
     hbuf = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    scr = torch.empty(4 * n, dtype=torch.uint8, device="cuda")
-    pd.pd_kv_pack_heads(desc, pool, b.num_pool_pages, pack_ids, 0, h1, hbuf, scr)
-    t = timed(lambda: pd.pd_kv_pack_heads(desc, pool, b.num_pool_pages, pack_ids, 0, h1, hbuf, scr),
-              args.phase_reps)
-    out["pack_heads"] = {"heads": [0, h1], "pages": n, "bytes": nb, "ms": round(t, 4),
-                         "GBps": round(2 * nb / (t * 1e-3) / 1e9, 1)}
-    t = timed(lambda: pd.pd_kv_unpack_heads(desc, pool, b.num_pool_pages, unpack_ids, 0, h1, hbuf, scr),
-              args.phase_reps)
-    out["unpack_heads"] = {"ms": round(t, 4), "GBps": round(2 * nb / (t * 1e-3) / 1e9, 1)}
+    r = meter.time(lambda: pd.pd_kv_pack_heads(desc, pool, b.num_pool_pages, pack_ids, 0, h1, hbuf, scr))
+    out["pack_heads"] = {"heads": [0, h1], "pages": n, "bytes": nb, "ms": r,
+                         "GBps": round(2 * nb / (r["median"] * 1e-3) / 1e9, 1)}
+    r = meter.time(lambda: pd.pd_kv_unpack_heads(desc, pool, b.num_pool_pages, unpack_ids, 0, h1, hbuf, scr))
+    out["unpack_heads"] = {"ms": r, "GBps": round(2 * nb / (r["median"] * 1e-3) / 1e9, 1)}
     del hbuf
 
     L = args.layers
@@ -204,12 +419,11 @@ def transfer_legs(args, pd, torch, b, desc, pool, pack_ids, unpack_ids):
     pd.pd_xfer_upload(x, ws)
     lbuf = torch.empty(x.buffer_bytes, dtype=torch.uint8, device="cuda")
     prog = torch.zeros(L, dtype=torch.int32, pin_memory=True)
-    pd.pd_kv_pack_layers(x, ws, lbuf, prog)
-    torch.cuda.synchronize()
-    t = timed(lambda: pd.pd_kv_pack_layers(x, ws, lbuf, prog), args.phase_reps)
+    r = meter.time(lambda: pd.pd_kv_pack_layers(x, ws, lbuf, prog))
     # the host polls the counters during one more launch (the launch returns
     # at once; the polling loop runs in this thread, so no lock stands between
     # the launch and the first read)
+    torch.cuda.synchronize()
     view = prog.numpy()
     start = view.copy()
     flips = [None] * L
@@ -224,8 +438,8 @@ def transfer_legs(args, pd, torch, b, desc, pool, pack_ids, unpack_ids):
     torch.cuda.synchronize()
     t_sync = time.perf_counter()
     ready = [round((f - t_launch) * 1e6, 1) if f is not None else None for f in flips]
-    out["pack_layers"] = {"layers": L, "pages_per_layer": n, "bytes": x.buffer_bytes, "ms": round(t, 4),
-                          "GBps": round(2 * x.buffer_bytes / (t * 1e-3) / 1e9, 1),
+    out["pack_layers"] = {"layers": L, "pages_per_layer": n, "bytes": x.buffer_bytes, "ms": r,
+                          "GBps": round(2 * x.buffer_bytes / (r["median"] * 1e-3) / 1e9, 1),
                           "host_seen_layer_ready_us": ready,
                           "host_launch_to_sync_us": round((t_sync - t_launch) * 1e6, 1)}
     x.close()
@@ -319,7 +533,7 @@ def interference_sweep(args, pd, torch):
     return res
 
 
-def mla_legs(args, pd, torch):
+def mla_legs(args, pd, torch, meter):
     """Latent-cache (MLA) decode legs, untimed by the step: the two DeepSeek
     decode workloads (one TP-8 rank with 16 query heads, one data-parallel
     attention rank with 128; 64 requests, caches of 1024..8192 tokens, page
@@ -330,21 +544,8 @@ def mla_legs(args, pd, torch):
     written (bytes); 2 (576 + 512) flops per (query row, visible key)."""
     from workloads import device_normal_, device_seed, make_mla_batch
 
-    reps = args.phase_reps * 4
-
     def timed(fn):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return float(np.median(ts))
+        return meter.time(fn)
 
     res = {}
     for name in ("mla_tp8", "mla_dp"):
@@ -359,8 +560,9 @@ def mla_legs(args, pd, torch):
         pd.pd_plan_upload(plan, ws)
         out = torch.empty((n, b.H, b.d_c), dtype=torch.float32, device="cuda")
         lse = torch.empty((n, b.H), dtype=torch.float32, device="cuda")
-        t_app = timed(lambda: pd.pd_mla_kv_append(plan, ws, pool, rows_new))
-        t_attn = timed(lambda: pd.pd_mla_attention_run(plan, ws, q, pool, out, lse))
+        r_app = timed(lambda: pd.pd_mla_kv_append(plan, ws, pool, rows_new))
+        r_attn = timed(lambda: pd.pd_mla_attention_run(plan, ws, q, pool, out, lse))
+        t_app, t_attn = r_app["median"], r_attn["median"]
         keys = int(b.kv_lens.astype(np.int64).sum())
         nbytes = keys * b.width * 2 + n * b.H * (b.width * 2 + b.d_c * 4 + 4)
         flops = keys * b.H * 2 * (b.width + b.d_c)           # qo = 1: every cached key is visible
@@ -370,18 +572,18 @@ def mla_legs(args, pd, torch):
         pb = pd.pd_mla_page_bytes(d)
         buf = torch.empty(len(ids) * pb, dtype=torch.uint8, device="cuda")
         scr = torch.empty(4 * len(ids), dtype=torch.uint8, device="cuda")
-        t_pack = timed(lambda: pd.pd_mla_kv_pack(d, pool, b.num_pool_pages, ids, buf, scr))
-        t_unpack = timed(lambda: pd.pd_mla_kv_unpack(d, pool, b.num_pool_pages, ids, buf, scr))
+        t_pack = timed(lambda: pd.pd_mla_kv_pack(d, pool, b.num_pool_pages, ids, buf, scr))["median"]
+        t_unpack = timed(lambda: pd.pd_mla_kv_unpack(d, pool, b.num_pool_pages, ids, buf, scr))["median"]
         st = plan.stats()
         res[name] = {
             "shape": f"B {b.B}, H {b.H}, latent {b.d_c} + rotary {b.d_r}, page {b.ps}, bf16, kv 1024..8192",
-            "attention_ms": round(t_attn, 4), "blocks": st.decode_units, "chunk_keys": st.decode_chunk_keys,
+            "attention_ms": r_attn, "blocks": st.decode_units, "chunk_keys": st.decode_chunk_keys,
             "GBps": round(nbytes / (t_attn * 1e-3) / 1e9, 1),
             "TFLOPs": round(flops / (t_attn * 1e-3) / 1e12, 1),
             "hbm_frac": round(nbytes / (t_attn * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "mfma_frac": round(flops / (t_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "roofline_frac": round(ideal / (t_attn * 1e-3), 4),
-            "append_us": round(t_app * 1e3, 2),
+            "append_ms": r_app,
             "pack_pages": len(ids), "pack_GBps": round(2 * len(ids) * pb / (t_pack * 1e-3) / 1e9, 1),
             "unpack_GBps": round(2 * len(ids) * pb / (t_unpack * 1e-3) / 1e9, 1),
         }
@@ -400,7 +602,7 @@ def main():
     import torch
 
     import decode_attention_kv_pd_amd as pd
-    from workloads import device_normal_, device_seed, make_batch
+    from workloads import make_batch
 
     torch.cuda.set_device(0)
     dev = "cuda"
@@ -412,12 +614,8 @@ def main():
     n_rows = int(b.qo_lens.sum())
 
     # ---- device-resident inputs
-    pool = device_normal_(torch.empty(b.pool_shape, dtype=torch.bfloat16, device=dev), device_seed(b.wid, 0, 0))
-    q = device_normal_(torch.empty((n_rows, b.H_q, b.D), dtype=torch.bfloat16, device=dev), device_seed(b.wid, 0, 1))
-    k_new = device_normal_(torch.empty((n_rows, b.H_kv, b.D), dtype=torch.bfloat16, device=dev), device_seed(b.wid, 0, 2))
-    v_new = device_normal_(torch.empty((n_rows, b.H_kv, b.D), dtype=torch.bfloat16, device=dev), device_seed(b.wid, 0, 3))
-    out = torch.empty((n_rows, b.H_q, b.D), dtype=torch.float32, device=dev)
-    lse = torch.empty((n_rows, b.H_q), dtype=torch.float32, device=dev)
+    t = device_inputs(torch, b, pd)
+    pool, q, k_new, v_new, out, lse = (t[k] for k in ("pool", "q", "k_new", "v_new", "out", "lse"))
     r_pack = int(np.argmax(b.qo_lens))
     pack_ids = b.request_pages(r_pack)
     unpack_ids = np.random.default_rng(7).permutation(b.spare_pages)[:len(pack_ids)].astype(np.int32)
@@ -428,7 +626,6 @@ def main():
     plan0 = pd.pd_plan(desc, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages)
     stats = plan0.stats()
     ws = torch.empty(plan0.workspace_bytes, dtype=torch.uint8, device=dev)
-    attn_bytes = work["decode_bytes"] + work["prefill_bytes"]
     assert stats.prefill_flops == work["prefill_flops"]
     torch.cuda.synchronize()
 
@@ -468,18 +665,23 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
-    def avg(a, c):
-        return float(np.mean([ev[i][a].elapsed_time(ev[i][c]) for i in range(args.steps)]))
+    def phase(a, c):
+        return spread([ev[i][a].elapsed_time(ev[i][c]) for i in range(args.steps)])
 
-    t_append, t_attn, t_pack, t_unpack = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    s_append, s_attn, s_pack, s_unpack = phase(0, 1), phase(1, 2), phase(2, 3), phase(3, 4)
+    t_attn = s_attn["mean"]     # average launch duration over the timed steps
     assert torch.isfinite(out).all().item(), "non-finite attention output"
+    print(f"[bench] timed steps: {ms_step:.4f} ms/step, attention launch avg {t_attn:.4f} ms",
+          file=sys.stderr, flush=True)
 
-    # ---- roofline of the dominant launch (pd_attention_run: mixed kernel + merge)
-    attn_hbm_ms = attn_bytes / (PEAK_HBM_GBPS * 1e9) * 1e3
+    # ---- roofline of the dominant launch (pd_attention_run: mixed kernel + merge).
+    # Algorithmic bytes: the decode requests' K/V read once, their Q read and
+    # O written; the prefill chunk's compulsory bytes are reported beside them.
+    attn_hbm_ms = work["decode_bytes"] / (PEAK_HBM_GBPS * 1e9) * 1e3
     attn_mfma_ms = work["prefill_flops"] / (PEAK_BF16_TFLOPS * 1e12) * 1e3
     bound = "hbm" if attn_hbm_ms >= attn_mfma_ms else "mfma"
     if bound == "hbm":
-        achieved, peak, unit = attn_bytes / (t_attn * 1e-3) / 1e9, PEAK_HBM_GBPS, "GB/s"
+        achieved, peak, unit = work["decode_bytes"] / (t_attn * 1e-3) / 1e9, PEAK_HBM_GBPS, "GB/s"
     else:
         achieved, peak, unit = work["prefill_flops"] / (t_attn * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     pack_bytes_rw = 2 * pack_nbytes
@@ -499,80 +701,66 @@ def main():
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.workload),
                      "kernel": "pd_attention_run (attn_bf16_kernel + merge_kernel)",
-                     "algorithmic_bytes": attn_bytes, "algorithmic_flops": work["prefill_flops"],
+                     "algorithmic_bytes": work["decode_bytes"],
+                     "prefill_compulsory_bytes": work["prefill_bytes"],
+                     "algorithmic_flops": work["prefill_flops"],
                      "mfma_frac": round(work["prefill_flops"] / (t_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "frac_sum_form": round((attn_hbm_ms + attn_mfma_ms) / t_attn, 4),
                      "avg_ms": round(t_attn, 4)},
-        "phases_ms": {"plan_host": round(plan_host_s * 1e3 / args.steps, 4), "append": round(t_append, 4),
-                      "attention": round(t_attn, 4), "pack": round(t_pack, 4), "unpack": round(t_unpack, 4)},
-        "append_GBps": round(work["append_bytes"] / (t_append * 1e-3) / 1e9, 1),
-        "pack_GBps": round(pack_bytes_rw / (t_pack * 1e-3) / 1e9, 1),
-        "unpack_GBps": round(pack_bytes_rw / (t_unpack * 1e-3) / 1e9, 1),
+        "phases_ms": {"plan_host": round(plan_host_s * 1e3 / args.steps, 4), "append": s_append,
+                      "attention": s_attn, "pack": s_pack, "unpack": s_unpack},
+        "append_GBps": round(work["append_bytes"] / (s_append["mean"] * 1e-3) / 1e9, 1),
+        "pack_GBps": round(pack_bytes_rw / (s_pack["mean"] * 1e-3) / 1e9, 1),
+        "unpack_GBps": round(pack_bytes_rw / (s_unpack["mean"] * 1e-3) / 1e9, 1),
         "plan": {"prefill_tiles": stats.prefill_tiles, "decode_units": stats.decode_units,
                  "decode_chunk_keys": stats.decode_chunk_keys},
     }
+    for p in keep:
+        p.close()
+    keep.clear()
+    meter = Meter(torch, args.reps, args.leg_warmup)
 
     # ---- per-phase legs: decode-only and prefill-only plans over the same pool
     if not args.no_phases:
-        dec = b.qo_lens * (b.H_q // b.H_kv) <= 16
+        dec = b.qo_lens == 1
         legs = {}
         for name, sel in (("decode_only", dec), ("prefill_only", ~dec)):
-            qo = np.where(sel, b.qo_lens, 0).astype(np.int32)
-            p = pd.pd_plan(desc, qo, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages)
-            wsp = torch.empty(max(p.workspace_bytes, 1), dtype=torch.uint8, device=dev)
-            pd.pd_plan_upload(p, wsp)
-            # rows of the selected requests only: pack their q rows first
-            idx = np.concatenate([np.arange(b.qo_indptr[r], b.qo_indptr[r + 1]) for r in range(b.B) if sel[r]])
-            qs = q[torch.as_tensor(idx, device=dev)].contiguous()
-            os_ = torch.empty((len(idx), b.H_q, b.D), dtype=torch.float32, device=dev)
-            ls = torch.empty((len(idx), b.H_q), dtype=torch.float32, device=dev)
-            pd.pd_attention_run(p, wsp, qs, pool, os_, ls)
-            torch.cuda.synchronize()
-            ts = []
-            for _ in range(args.phase_reps):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                pd.pd_attention_run(p, wsp, qs, pool, os_, ls)
-                e1.record()
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1))
-            t = float(np.median(ts))
+            p, wsp, qs, os_, ls = sub_plan(pd, torch, b, desc, sel, q)
+            r = meter.time(lambda: pd.pd_attention_run(p, wsp, qs, pool, os_, ls))
+            tm = r["median"]
             if name == "decode_only":
-                gbps = work["decode_bytes"] / (t * 1e-3) / 1e9
-                legs[name] = {"ms": round(t, 4), "GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+                gbps = work["decode_bytes"] / (tm * 1e-3) / 1e9
+                r.update({"GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)})
             else:
-                tf = work["prefill_flops"] / (t * 1e-3) / 1e12
-                legs[name] = {"ms": round(t, 4), "TFLOPs": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                tf = work["prefill_flops"] / (tm * 1e-3) / 1e12
+                r.update({"TFLOPs": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+            legs[name] = r
             p.close()
             del wsp, qs, os_, ls
         # the same mixed batch with every prefill tile launched before the decode blocks
-        p = pd.pd_plan(desc, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages,
-                       block_order=1)
-        pd.pd_plan_upload(p, ws)
-        pd.pd_attention_run(p, ws, q, pool, out, lse)
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(args.phase_reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            pd.pd_attention_run(p, ws, q, pool, out, lse)
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        legs["mixed_prefill_first_order_ms"] = round(float(np.median(ts)), 4)
+        p, wsp, qs, os_, ls = sub_plan(pd, torch, b, desc, np.ones(b.B, bool), q, block_order=1)
+        legs["mixed_prefill_first_order_ms"] = meter.time(lambda: pd.pd_attention_run(p, wsp, qs, pool, os_, ls))
         p.close()
-        legs["interference_ratio"] = round(t_attn / legs["decode_only"]["ms"], 3)
-        legs["mixed_vs_sum"] = round(t_attn / (legs["decode_only"]["ms"] + legs["prefill_only"]["ms"]), 3)
+        del wsp, qs, os_, ls
+        legs["interference_ratio"] = round(t_attn / legs["decode_only"]["median"], 3)
+        legs["mixed_vs_sum"] = round(t_attn / (legs["decode_only"]["median"] + legs["prefill_only"]["median"]), 3)
         result["phases"] = legs
         result["decode_attn_GBps"] = legs["decode_only"]["GBps"]
         result["prefill_attn_TFLOPs"] = legs["prefill_only"]["TFLOPs"]
         print(f"[bench] phase legs done", file=sys.stderr, flush=True)
 
     if not args.no_transfers:
-        result["transfers"] = transfer_legs(args, pd, torch, b, desc, pool, pack_ids, unpack_ids)
+        result["transfers"] = transfer_legs(args, pd, torch, meter, b, desc, pool, pack_ids, unpack_ids)
         print(f"[bench] transfer legs done", file=sys.stderr, flush=True)
 
+    del t, pool, q, k_new, v_new, out, lse, buf, scratch, ws
+    torch.cuda.synchronize()
+
+    if not args.no_configs:
+        result["workloads"] = config_legs(args, pd, torch, meter)
+
     if not args.no_mla:
-        result["mla_decode"] = mla_legs(args, pd, torch)
+        result["mla_decode"] = mla_legs(args, pd, torch, meter)
         print(f"[bench] MLA legs done", file=sys.stderr, flush=True)
 
     if not args.no_sweep:
@@ -581,7 +769,7 @@ def main():
 
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(b, args.cpu_decode_requests, args.cpu_prefill_tokens)
+        result["cpu_baseline"] = cpu_baseline(b, args.cpu_workers, args.cpu_decode_rows, args.cpu_prefill_rows)
 
     print(json.dumps(result), flush=True)
 
