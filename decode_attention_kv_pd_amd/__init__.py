@@ -9,6 +9,7 @@ The names mirror the C entry points of include/pd_attn.h:
   pd_plan_upload(plan, ws, stream=None)
   pd_kv_append(plan, ws, kv_pool, k_new, v_new, stream=None)
   pd_attention_run(plan, ws, q, kv_pool, out, lse=None, stream=None)
+  pd_attention_run_noalloc(plan, q, kv_pool, out, lse=None, k_new=None, v_new=None, stream=None)
   pd_kv_pack_bytes(desc, n_pages)                   -> int
   pd_kv_pack(desc, kv_pool, num_pool_pages, page_ids, buf, scratch, stream=None)
   pd_kv_unpack(desc, kv_pool, num_pool_pages, page_ids, buf, scratch, stream=None)
@@ -87,7 +88,7 @@ class pd_plan_stats(ctypes.Structure):
 
 
 EXPORTS = ("pd_plan", "pd_plan_workspace_bytes", "pd_plan_upload", "pd_plan_get_stats",
-           "pd_plan_free", "pd_plan_work_items", "pd_kv_append", "pd_attention_run", "pd_kv_pack_bytes",
+           "pd_plan_free", "pd_plan_work_items", "pd_kv_append", "pd_attention_run", "pd_attention_run_noalloc", "pd_kv_pack_bytes",
            "pd_kv_pack", "pd_kv_unpack", "pd_kv_pack_heads_bytes", "pd_kv_pack_heads", "pd_kv_unpack_heads",
            "pd_kv_shard_transfers", "pd_xfer_plan", "pd_xfer_buffer_bytes", "pd_xfer_workspace_bytes",
            "pd_xfer_upload", "pd_kv_pack_layers", "pd_kv_unpack_layers", "pd_xfer_free",
@@ -119,6 +120,7 @@ def _load():
         "pd_plan_work_items": (I32, [P, I32, pI32, I32]),
         "pd_kv_append": (I32, [P, VP, VP, VP, VP, VP]),
         "pd_attention_run": (I32, [P, VP, VP, VP, VP, VP, VP]),
+        "pd_attention_run_noalloc": (I32, [P, VP, VP, VP, VP, VP, VP, VP]),
         "pd_kv_pack_bytes": (SZ, [ctypes.POINTER(pd_attn_desc), I32]),
         "pd_kv_pack": (I32, [ctypes.POINTER(pd_attn_desc), VP, I32, pI32, I32, VP, SZ, VP, SZ, VP]),
         "pd_kv_unpack": (I32, [ctypes.POINTER(pd_attn_desc), VP, I32, pI32, I32, VP, SZ, VP, SZ, VP]),
@@ -293,6 +295,17 @@ def pd_kv_append(plan: Plan, ws, kv_pool, k_new, v_new, stream=None):
 def pd_attention_run(plan: Plan, ws, q, kv_pool, out, lse=None, stream=None):
     _check(_lib.pd_attention_run(plan.handle, _dev(ws, "ws"), _dev(q, "q"), _dev(kv_pool, "kv_pool"),
                                  _dev(out, "out"), _dev(lse, "lse"), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024   # PD_NOALLOC_SCRATCH_BYTES
+
+
+def pd_attention_run_noalloc(plan: Plan, q, kv_pool, out, lse=None, k_new=None, v_new=None, stream=None):
+    """pd_attention_run (after pd_kv_append when k_new / v_new are given)
+    over the library's static device scratch: no workspace, no upload."""
+    _check(_lib.pd_attention_run_noalloc(plan.handle, _dev(q, "q"), _dev(kv_pool, "kv_pool"),
+                                         _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(out, "out"),
+                                         _dev(lse, "lse"), _stream(stream)))
 
 
 def pd_kv_pack_bytes(desc, n_pages: int) -> int:

@@ -17,7 +17,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpd_attn.so")
-SOURCES = [os.path.join(HERE, "csrc", n) for n in ("api.cpp", "attention.hip", "mla.hip", "mla_wide.hip", "kv_ops.hip")]
+SOURCES = [os.path.join(HERE, "csrc", n) for n in ("api.cpp", "attention.hip", "mla.hip", "mla_wide.hip", "kv_ops.hip", "noalloc.hip")]
 ARCH = "gfx950"
 
 

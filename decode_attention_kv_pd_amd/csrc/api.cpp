@@ -26,6 +26,7 @@
 
 #include "pd_attn.h"
 #include "pd_internal.hpp"
+#include "host_internal.hpp"
 
 namespace {
 
@@ -767,6 +768,60 @@ pd_status xfer_layers(pd_xfer_t x, void* d_ws, const void* d_buf, size_t buf_byt
 }
 }  // namespace
 
+namespace pdh {
+
+pd_status set_error(pd_status s, const char* msg) { return fail(s, msg); }
+
+pd_status hip_error(hipError_t e, const char* what) { return hip_fail(e, what); }
+
+PlanImage plan_image(pd_plan_t plan) {
+  PlanImage im{};
+  im.tables = plan->blob.data();
+  im.table_bytes = plan->meta_bytes;
+  im.ws_bytes = plan->ws_bytes;
+  im.mla = plan->mla;
+  im.total_rows = plan->total_rows;
+  return im;
+}
+
+pd_status enqueue_append(pd_plan_t plan, void* d_ws, void* kv_pool, const void* k_new, const void* v_new,
+                         void* stream) {
+  char* ws = (char*)d_ws;
+  pdk::AppendParams p{};
+  p.pool = kv_pool;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.qo_indptr = (const int32_t*)(ws + plan->off_qo);
+  p.req = (const pdk::ReqInfo*)(ws + plan->off_req);
+  p.page_indices = (const int32_t*)(ws + plan->off_pages);
+  p.B = plan->B;
+  p.total_rows = plan->total_rows;
+  p.H_kv = plan->desc.num_kv_heads;
+  p.ps = plan->desc.page_size;
+  p.D = plan->desc.head_dim;
+  p.elt = elt_bytes(&plan->desc);
+  hipError_t e = pdk::launch_append(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return PD_OK;
+}
+
+pd_status enqueue_attention(pd_plan_t plan, void* d_ws, const void* q, const void* kv_pool, float* out, float* lse,
+                            void* stream) {
+  pdk::AttnParams a = attn_params(*plan, d_ws);
+  a.q = q;
+  a.pool = kv_pool;
+  a.out = out;
+  a.lse = lse;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = pdk::launch_attention(a, plan->desc.dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  e = pdk::launch_merge(a, st);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return PD_OK;
+}
+
+}  // namespace pdh
+
 extern "C" {
 
 pd_status pd_plan(const pd_attn_desc* desc, int32_t batch, const int32_t* qo_lens, const int32_t* kv_lens,
@@ -881,23 +936,7 @@ pd_status pd_kv_append(pd_plan_t plan, void* d_ws, void* kv_pool, const void* k_
   if (plan->mla) return fail(PD_ERR_INVALID_ARG, "an MLA plan: use pd_mla_kv_append");
   if (plan->total_rows == 0) return PD_OK;
   if (!kv_pool || !k_new || !v_new) return fail(PD_ERR_INVALID_ARG, "NULL pool or K/V pointer");
-  char* ws = (char*)d_ws;
-  pdk::AppendParams p{};
-  p.pool = kv_pool;
-  p.k_new = k_new;
-  p.v_new = v_new;
-  p.qo_indptr = (const int32_t*)(ws + plan->off_qo);
-  p.req = (const pdk::ReqInfo*)(ws + plan->off_req);
-  p.page_indices = (const int32_t*)(ws + plan->off_pages);
-  p.B = plan->B;
-  p.total_rows = plan->total_rows;
-  p.H_kv = plan->desc.num_kv_heads;
-  p.ps = plan->desc.page_size;
-  p.D = plan->desc.head_dim;
-  p.elt = elt_bytes(&plan->desc);
-  hipError_t e = pdk::launch_append(p, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "append launch");
-  return PD_OK;
+  return pdh::enqueue_append(plan, d_ws, kv_pool, k_new, v_new, stream);
 }
 
 pd_status pd_attention_run(pd_plan_t plan, void* d_ws, const void* q, const void* kv_pool, float* out,
@@ -906,17 +945,7 @@ pd_status pd_attention_run(pd_plan_t plan, void* d_ws, const void* q, const void
   if (plan->mla) return fail(PD_ERR_INVALID_ARG, "an MLA plan: use pd_mla_attention_run");
   if (plan->total_rows == 0) return PD_OK;
   if (!q || !kv_pool || !out) return fail(PD_ERR_INVALID_ARG, "NULL q, pool or out");
-  pdk::AttnParams a = attn_params(*plan, d_ws);
-  a.q = q;
-  a.pool = kv_pool;
-  a.out = out;
-  a.lse = lse;
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e = pdk::launch_attention(a, plan->desc.dtype, st);
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
-  e = pdk::launch_merge(a, st);
-  if (e != hipSuccess) return hip_fail(e, "merge launch");
-  return PD_OK;
+  return pdh::enqueue_attention(plan, d_ws, q, kv_pool, out, lse, stream);
 }
 
 size_t pd_kv_pack_bytes(const pd_attn_desc* desc, int32_t n_pages) {

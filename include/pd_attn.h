@@ -490,6 +490,36 @@ pd_status pd_mla_kv_unpack(const pd_mla_desc* desc, void* kv_pool,
                            void* d_scratch, size_t scratch_bytes,
                            void* stream);
 
+/* ---- For callers that cannot allocate --------------------------------
+ * pd_attention_run_noalloc is pd_attention_run, optionally preceded by
+ * pd_kv_append, for callers that cannot allocate device memory or pinned host
+ * memory per step: serving loops that forbid hipMalloc, harnesses that run
+ * with a fixed memory budget.  It needs no workspace argument and no
+ * pd_plan_upload: the plan's tables and the split-KV partial results go to a
+ * static device buffer of PD_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends.  The call allocates nothing.
+ *   plan         a pd_plan (not an MLA plan) whose pd_plan_workspace_bytes
+ *                is <= PD_NOALLOC_SCRATCH_BYTES
+ *   q, kv_pool, out, lse   as pd_attention_run (lse may be NULL)
+ *   k_new, v_new both NULL: attention only; both non-NULL: the append of
+ *                pd_kv_append runs first, on the same stream
+ * The tables are copied from the plan's host memory with a host-to-device
+ * copy on `stream` (pageable memory: the copy has read them when the call
+ * returns), so a HIP graph cannot capture this call.  Every call on one GPU
+ * uses that GPU's one buffer: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller;
+ * calls on one stream are ordered.  Nothing in the buffer has to start at
+ * zero: each call rewrites the tables and every partial result is written
+ * before it is read.
+ * Errors: PD_ERR_INVALID_ARG (NULL plan, an MLA plan, only one of k_new /
+ * v_new, NULL q / pool / out), PD_ERR_WORKSPACE (the plan needs more than
+ * PD_NOALLOC_SCRATCH_BYTES), PD_ERR_HIP; all checked before anything is
+ * enqueued. */
+#define PD_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+pd_status pd_attention_run_noalloc(pd_plan_t plan, const void* q, void* kv_pool,
+                                   const void* k_new, const void* v_new,
+                                   float* out, float* lse, void* stream);
+
 /* Static text for a status code. */
 const char* pd_status_string(pd_status s);
 

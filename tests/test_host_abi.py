@@ -1,6 +1,7 @@
 """C-ABI boundary on the CPU: the library loads, exports every entry point the
 header declares, rejects bad input with the documented status before doing
 any device work, and the planner's work list covers the batch exactly."""
+import ctypes
 import os
 import re
 
@@ -323,3 +324,32 @@ def test_decode_chunk_option_near_int32_max_still_covers_every_row(chunk):
     assert (mg[:, 3] >= 1).all()
     s = plan.stats()
     assert 32 <= s.decode_chunk_keys <= 4096 + 31
+
+
+# ------------------------------------------------- the no-allocation call
+def test_noalloc_rejects_before_any_device_work():
+    """Checks that need no device: an oversized plan, an MLA plan and a lone
+    k_new are refused with the documented status before anything runs."""
+    b = make_batch("long", materialize=False)
+    d = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype, b.causal)
+    big = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages,
+                     decode_chunk_keys=32)
+    assert big.workspace_bytes > pd.NOALLOC_SCRATCH_BYTES
+    expect("PD_ERR_WORKSPACE", pd.pd_attention_run_noalloc, big, None, None, None, stream=0)
+    fits = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages)
+    assert fits.workspace_bytes <= pd.NOALLOC_SCRATCH_BYTES   # the long workload fits
+    st = pd._lib.pd_attention_run_noalloc(fits.handle, None, None, ctypes.c_void_p(256), None, None, None, None)
+    assert pd.STATUS[st] == "PD_ERR_INVALID_ARG"
+    from workloads import make_mla_batch
+    m = make_mla_batch("mla_tiny", materialize=False)
+    md = pd.make_mla_desc(m.H, m.ps, m.causal, m.sm_scale)
+    mp = pd.pd_mla_plan(md, m.qo_lens, m.kv_lens, m.page_indptr, m.page_indices, m.num_pool_pages)
+    expect("PD_ERR_INVALID_ARG", pd.pd_attention_run_noalloc, mp, None, None, None, stream=0)
+    assert pd.STATUS[pd._lib.pd_attention_run_noalloc(None, None, None, None, None, None, None, None)] == \
+        "PD_ERR_INVALID_ARG"
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define PD_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", text)
+    assert m and int(m.group(1)) * 2 ** 20 == pd.NOALLOC_SCRATCH_BYTES
