@@ -28,7 +28,7 @@ Afterwards, untimed legs measure:
     workloads;
   * transfers, the interference sweep and the latent-cache decode;
   * the CPU oracle on a bounded sample, over a process pool.
-Every leg times one call per repetition with HIP events after streaming a
+Every leg times one call per repetition with HIP events after reading a
 1 GiB buffer (so L2 and MALL start cold), and reports median, min and p90;
 calls shorter than 50 us are also timed as 100 back-to-back launches.
 
@@ -143,11 +143,14 @@ class Meter:
         self.torch = torch
         self.reps = reps
         self.warmup = warmup
-        self.flush_buf = torch.zeros(flush_bytes // 4, dtype=torch.int32, device="cuda")
+        self.flush_buf = torch.ones(flush_bytes // 4, dtype=torch.int32, device="cuda")
+        self.flush_out = torch.empty((), dtype=torch.int64, device="cuda")
 
     def flush(self):
-        # reads and writes 1 GiB: evicts the L2 of every XCD and the MALL
-        self.flush_buf.add_(1)
+        # reads 1 GiB (a sum): replaces the L2 of every XCD and the MALL with
+        # clean lines, so the timed call neither hits its own data nor pays for
+        # writing back someone else's
+        self.torch.sum(self.flush_buf, 0, dtype=self.torch.int64, out=self.flush_out)
 
     def time(self, fn, flush=True, b2b=None):
         torch = self.torch
@@ -376,6 +379,41 @@ def config_legs(args, pd, torch, meter):
         del t, ws
         torch.cuda.synchronize()
         print(f"[bench] {wid} workload leg done", file=sys.stderr, flush=True)
+    res["wide_decode"] = wide_decode_legs(pd, torch, meter)
+    return res
+
+
+def wide_decode_legs(pd, torch, meter):
+    """Decode rows of more than 16 query rows per KV head (post, sections
+    "Speculative Decoding": multi-token steps, and "Prefill vs Decode
+    performance": decode spread over kv_len): 64 requests over 16384-token
+    caches, 8 KV heads, head_dim 128, page 64, bf16, with 32 query heads per
+    KV head (g = 32), 64 (g = 64), and 4-token steps at g = 8 (32 rows).
+    Algorithmic bytes: K/V read once plus Q and O."""
+    from workloads import make_batch
+
+    res = {}
+    for name, heads, qo in (("g32", (256, 8), 1), ("g64", (512, 8), 1), ("qo4_g8", (64, 8), 4)):
+        n = 64
+        b = make_batch("long", lengths=([qo] * n, [16384] * n), heads=heads, materialize=False)
+        desc = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype, b.causal, b.sm_scale)
+        t = device_inputs(torch, b, pd, salt=7)
+        plan = pd.pd_plan(desc, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages)
+        ws = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device="cuda")
+        pd.pd_plan_upload(plan, ws)
+        r = meter.time(lambda: pd.pd_attention_run(plan, ws, t["q"], t["pool"], t["out"], t["lse"]))
+        assert torch.isfinite(t["out"]).all().item(), f"{name}: non-finite attention output"
+        nbytes = 2 * int(b.kv_lens.astype(np.int64).sum()) * b.H_kv * b.D * 2 + int(b.qo_lens.sum()) * b.H_q * b.D * 6
+        gbps = nbytes / (r["median"] * 1e-3) / 1e9
+        st = plan.stats()
+        res[name] = {"shape": f"64 x (qo {qo}, kv 16384), H {b.H_q}/{b.H_kv} (rows per KV head {qo * b.H_q // b.H_kv})",
+                     "ms": r, "bytes": nbytes, "GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                     "decode_units": st.decode_units, "prefill_tiles": st.prefill_tiles,
+                     "chunk_keys": st.decode_chunk_keys}
+        plan.close()
+        del t, ws
+        torch.cuda.synchronize()
+    print(f"[bench] wide decode legs done", file=sys.stderr, flush=True)
     return res
 
 

@@ -242,9 +242,9 @@ class Plan:
 
     def work_items(self, kind: int) -> np.ndarray:
         """The plan's work list: kind 0 prefill tiles [n, 8], 1 decode units
-        [n, 8], 2 merge groups [n, 4], 3 launch block map [n, 1] (see
-        pd_plan_work_items)."""
-        width = {0: 8, 1: 8, 2: 4, 3: 1}.get(int(kind), 8)
+        [n, 8], 2 merge groups [n, 4], 3 launch block map [n, 1], 4 decode
+        queue offsets [n, 1] (see pd_plan_work_items)."""
+        width = {0: 8, 1: 8, 2: 4, 3: 1, 4: 1}.get(int(kind), 8)
         n = _lib.pd_plan_work_items(self.handle, int(kind), None, 0)
         if n < 0:
             _check(n)

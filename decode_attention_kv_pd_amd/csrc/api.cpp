@@ -97,10 +97,11 @@ struct pd_plan_s {
   std::vector<pdk::ReqInfo> req;
   std::vector<int32_t> pages;
   std::vector<pdk::PrefillItem> pf;
-  std::vector<pdk::DecodeItem> du;
+  std::vector<pdk::DecodeItem> du;  // in queue order
+  std::vector<int32_t> dq;          // wave slot s runs units [dq[s], dq[s + 1])
   std::vector<pdk::MergeGroup> mg;
   std::vector<int32_t> block_map;  // attention launch order
-  size_t off_qo = 0, off_req = 0, off_pages = 0, off_pf = 0, off_du = 0, off_mg = 0, off_bmap = 0;
+  size_t off_qo = 0, off_req = 0, off_pages = 0, off_pf = 0, off_du = 0, off_dq = 0, off_mg = 0, off_bmap = 0;
   size_t meta_bytes = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   int64_t prefill_flops = 0, decode_bytes = 0;
   std::vector<char> blob;  // host image of the workspace tables
@@ -201,6 +202,155 @@ int equal_chunk_len(int32_t kv, int chunk) {
   return (int)std::min<int64_t>(round_up32(((int64_t)kv + nch - 1) / nch), (int64_t)1 << 30);
 }
 
+// ---- decode role planning.
+// A (request, KV head) whose qo * g query rows fit kMaxDecodeRows is a decode
+// row group.  Rows <= 16: one wavefront with one 16-row column group; <= 32:
+// one wavefront with two; <= 64: two wavefronts of one block side by side
+// (rows [0, 32) and [32, 64)) on the same keys, so the second read of every
+// key hits the cache.  A piece of a group over keys [k0, k1) (k0 a multiple
+// of 32) is a unit; a wavefront runs a queue of units back to back.
+//   * Few prefill tiles (one dispatch round): the groups of a class are laid
+//     end to end (each padded to a multiple of 32 keys) and cut into equal
+//     spans, one per queue, so every queue streams the same number of keys
+//     and changes row group (reloading its Q) only where a span crosses a
+//     group boundary.
+//   * Many prefill tiles: every group is cut into equal chunks of about
+//     decode_chunk_keys, each its own queue, and the decode blocks
+//     interleave with the prefill tiles.
+// Partial results: piece i of a group of `rows` rows owns the partial rows
+// [part0 + i rows, part0 + (i + 1) rows).
+struct DecodeGroup {
+  int r, hk, rows, cls;  // cls 0: rows <= 16; 1: rows <= 32; 2: rows <= 64
+  int part0;
+  std::vector<std::pair<int, int>> pieces;  // key ranges, in key order
+};
+constexpr int kClsWidth[3] = {1, 1, 2};  // wavefronts per queue
+constexpr int kClsNcg[3] = {1, 2, 2};    // 16-row column groups per wavefront
+constexpr int kMinSpanKeys = 256;        // shortest span worth a queue
+
+pd_status build_decode(pd_plan_s& P, const pd_plan_options* opts, int num_cus, int n_prefill_tiles,
+                       std::vector<double>& block_cost) {
+  const pd_attn_desc& d = P.desc;
+  const int g = P.g, H_kv = d.num_kv_heads, D = d.head_dim, elt = elt_bytes(&d);
+  std::vector<DecodeGroup> groups;
+  int64_t class_keys[3] = {0, 0, 0};  // padded to multiples of 32 per group
+  for (int r = 0; r < P.B; ++r) {
+    const pdk::ReqInfo& ri = P.req[r];
+    const int64_t rows = (int64_t)ri.qo * g;
+    if (ri.qo == 0 || rows > pdk::kMaxDecodeRows) continue;
+    const int cls = rows <= 16 ? 0 : rows <= 32 ? 1 : 2;
+    for (int hk = 0; hk < H_kv; ++hk) groups.push_back({r, hk, (int)rows, cls, 0, {}});
+    class_keys[cls] += round_up32(ri.kv) * H_kv;
+    P.decode_bytes += 2LL * ri.kv * H_kv * D * elt;
+  }
+  P.chunk_keys = 0;
+  P.dq.assign(1, 0);
+  if (groups.empty()) return PD_OK;
+  const int64_t wave_keys = class_keys[0] + class_keys[1] + 2 * class_keys[2];
+  // queues: each a list of (group, piece) in stream order
+  struct QEntry {
+    int grp, piece;
+  };
+  std::vector<std::vector<QEntry>> queues[3];
+  const bool one_round = n_prefill_tiles < num_cus && !(opts && opts->decode_chunk_keys > 0);
+  if (one_round) {
+    const int slots =
+        pdk::kWavesPerBlock * (n_prefill_tiles == 0 ? num_cus : std::max(num_cus - n_prefill_tiles, num_cus / 2));
+    int lanes[3] = {0, 0, 0};
+    int used = 0;
+    for (int c = 0; c < 3; ++c) {
+      if (!class_keys[c]) continue;
+      const double share = (double)class_keys[c] * kClsWidth[c] / (double)wave_keys;
+      lanes[c] = std::max(1, (int)(share * slots / kClsWidth[c]));
+      lanes[c] = (int)std::min<int64_t>(lanes[c], std::max<int64_t>(1, class_keys[c] / kMinSpanKeys));
+      used += lanes[c] * kClsWidth[c];
+    }
+    for (int c = 2; used > slots && c >= 0; --c)  // rounding overshoot: trim the widest classes
+      while (used > slots && lanes[c] > 1) --lanes[c], used -= kClsWidth[c];
+    for (int c = 0; c < 3; ++c) {
+      if (!lanes[c]) continue;
+      const int64_t steps = class_keys[c] / 32;            // 32-key steps of the class
+      const int64_t per = (steps + lanes[c] - 1) / lanes[c];  // steps per queue
+      queues[c].assign((size_t)((steps + per - 1) / per), {});
+      int64_t pos = 0;  // first step of the current group in the class's stream
+      for (size_t gi = 0; gi < groups.size(); ++gi) {
+        DecodeGroup& gr = groups[gi];
+        if (gr.cls != c) continue;
+        const int kv = P.req[gr.r].kv;
+        const int64_t gsteps = round_up32(kv) / 32;
+        for (int64_t s = 0; s < gsteps;) {
+          const int64_t q = (pos + s) / per;  // queue of this step
+          const int64_t e = std::min(gsteps, (q + 1) * per - pos);
+          gr.pieces.push_back({(int)(s * 32), (int)std::min<int64_t>(kv, e * 32)});
+          queues[c][q].push_back({(int)gi, (int)gr.pieces.size() - 1});
+          s = e;
+        }
+        pos += gsteps;
+      }
+    }
+  } else {
+    int chunk;
+    if (opts && opts->decode_chunk_keys > 0) {
+      chunk = clamp_chunk_option(opts->decode_chunk_keys, P);
+    } else {
+      const int64_t target_units = (int64_t)num_cus * 16;
+      int64_t c = (wave_keys + target_units - 1) / target_units;
+      c = (c + 255) / 256 * 256;
+      chunk = (int)std::min<int64_t>(std::max<int64_t>(c, 256), 16384);
+    }
+    P.chunk_keys = chunk;
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      DecodeGroup& gr = groups[gi];
+      const int kv = P.req[gr.r].kv;
+      const int len = equal_chunk_len(kv, chunk);
+      for (int64_t k0 = 0; k0 < kv; k0 += len) {
+        gr.pieces.push_back({(int)k0, (int)std::min<int64_t>(kv, k0 + len)});
+        queues[gr.cls].push_back({{(int)gi, (int)gr.pieces.size() - 1}});
+      }
+    }
+    for (int c = 0; c < 3; ++c)  // longest first
+      std::stable_sort(queues[c].begin(), queues[c].end(), [&](const std::vector<QEntry>& x, const std::vector<QEntry>& y) {
+        const auto& px = groups[x[0].grp].pieces[x[0].piece];
+        const auto& py = groups[y[0].grp].pieces[y[0].piece];
+        return (px.second - px.first) > (py.second - py.first);
+      });
+  }
+  // partial rows and merge groups
+  int64_t n_parts = 0;
+  for (DecodeGroup& gr : groups) {
+    if (gr.pieces.empty() || n_parts + (int64_t)gr.pieces.size() * gr.rows > kMaxParts)
+      return fail(PD_ERR_UNSUPPORTED, "more than 2^26 split-KV partial result rows");
+    gr.part0 = (int)n_parts;
+    n_parts += (int64_t)gr.pieces.size() * gr.rows;
+    P.mg.push_back({gr.r, gr.hk, gr.part0, (int)gr.pieces.size()});
+  }
+  P.n_parts = (int32_t)n_parts;
+  if (!P.chunk_keys) {  // report the longest unit
+    for (const DecodeGroup& gr : groups)
+      for (const auto& pc : gr.pieces) P.chunk_keys = std::max(P.chunk_keys, pc.second - pc.first);
+  }
+  // wavefront slots: class-2 queues take an aligned pair of wavefronts of one
+  // block (the two 32-row halves side by side), then the others
+  std::vector<std::pair<int, int>> slot_queue;  // (class, queue) per slot; c0 of a class-2 slot by parity
+  for (int q = 0; q < (int)queues[2].size(); ++q) slot_queue.push_back({2, q}), slot_queue.push_back({2, q});
+  for (int c = 0; c < 2; ++c)
+    for (int q = 0; q < (int)queues[c].size(); ++q) slot_queue.push_back({c, q});
+  const int n_slots = (int)slot_queue.size();
+  block_cost.assign((n_slots + pdk::kWavesPerBlock - 1) / pdk::kWavesPerBlock, 0.0);
+  for (int s = 0; s < n_slots; ++s) {
+    const int c = slot_queue[s].first, q = slot_queue[s].second;
+    const int c0 = (c == 2 && (s & 1)) ? 32 : 0;
+    for (const QEntry& e : queues[c][q]) {
+      const DecodeGroup& gr = groups[e.grp];
+      const auto& pc = gr.pieces[e.piece];
+      P.du.push_back({gr.r, gr.hk, pc.first, pc.second, gr.part0 + e.piece * gr.rows + c0, c0, kClsNcg[c], 0});
+      block_cost[s / pdk::kWavesPerBlock] += 2.0 * (pc.second - pc.first) * D * elt;
+    }
+    P.dq.push_back((int32_t)P.du.size());
+  }
+  return PD_OK;
+}
+
 pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   const pd_attn_desc& d = P.desc;
   const int g = P.g;
@@ -208,7 +358,7 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   const int64_t elt = elt_bytes(&d);
   int num_cus = (opts && opts->num_cus > 0) ? opts->num_cus : 256;
 
-  // ---- prefill tiles: requests whose qo * g rows exceed one decode unit
+  // ---- prefill tiles: requests whose qo * g rows exceed the decode role's
   const int T = std::max(1, pdk::kPrefillRows / g);  // tokens per tile
   std::vector<double> pf_cost;                        // flops of each tile, launch order
   struct Tile {
@@ -218,7 +368,7 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   std::vector<std::vector<Tile>> groups;  // per (request, kv head)
   for (int r = 0; r < P.B; ++r) {
     const pdk::ReqInfo& ri = P.req[r];
-    if (ri.qo == 0 || (int64_t)ri.qo * g <= pdk::kDecodeCols) continue;
+    if (ri.qo == 0 || (int64_t)ri.qo * g <= pdk::kMaxDecodeRows) continue;
     const int64_t pairs = (int64_t)ri.qo * (ri.kv - ri.qo) + (int64_t)ri.qo * (ri.qo + 1) / 2;
     P.prefill_flops += 4LL * d.head_dim * d.num_qo_heads * (d.causal ? pairs : (int64_t)ri.qo * ri.kv);
     for (int hk = 0; hk < H_kv; ++hk) {
@@ -269,46 +419,12 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
     }
   }
 
-  // ---- decode units: requests with qo * g <= 16
-  int64_t decode_keys = 0;
-  for (int r = 0; r < P.B; ++r) {
-    const pdk::ReqInfo& ri = P.req[r];
-    if (ri.qo == 0 || (int64_t)ri.qo * g > pdk::kDecodeCols) continue;
-    decode_keys += (int64_t)ri.kv * H_kv;
-    P.decode_bytes += 2LL * ri.kv * H_kv * d.head_dim * elt;
-  }
-  int chunk = 0;
-  if (opts && opts->decode_chunk_keys > 0) {
-    chunk = clamp_chunk_option(opts->decode_chunk_keys, P);
-  } else if (decode_keys > 0) {
-    const int64_t target_units = (int64_t)num_cus * 16;
-    int64_t c = (decode_keys + target_units - 1) / target_units;
-    c = (c + 255) / 256 * 256;
-    chunk = (int)std::min<int64_t>(std::max<int64_t>(c, 256), 16384);
-  }
-  P.chunk_keys = chunk;
-  std::vector<pdk::DecodeItem> units;
-  for (int r = 0; r < P.B; ++r) {
-    const pdk::ReqInfo& ri = P.req[r];
-    if (ri.qo == 0 || (int64_t)ri.qo * g > pdk::kDecodeCols) continue;
-    const int len = equal_chunk_len(ri.kv, chunk);
-    const int nch = (int)(((int64_t)ri.kv + len - 1) / len);
-    if ((int64_t)P.n_parts + (int64_t)nch * H_kv > kMaxParts)
-      return fail(PD_ERR_UNSUPPORTED, "more than 2^26 split-KV decode units");
-    for (int hk = 0; hk < H_kv; ++hk) {
-      P.mg.push_back({r, hk, P.n_parts, nch});
-      for (int c = 0; c < nch; ++c) {
-        const int k0 = (int)((int64_t)c * len), k1 = (int)std::min<int64_t>(ri.kv, (int64_t)k0 + len);
-        units.push_back({r, hk, k0, k1, P.n_parts++, 0, 0, 0});
-      }
-    }
-  }
-  for (const pdk::MergeGroup& m : P.mg)
-    if (m.nparts < 1) return fail(PD_ERR_INVALID_ARG, "planner: a decode row group without a key chunk");
-  std::stable_sort(units.begin(), units.end(), [](const pdk::DecodeItem& a, const pdk::DecodeItem& b) {
-    return (a.k1 - a.k0) > (b.k1 - b.k0);
-  });
-  P.du = std::move(units);
+  // ---- decode units: (request, KV head) row groups of at most kMaxDecodeRows
+  // query rows, each cut into key chunks; units go to per-wavefront queues
+  std::vector<double> db_cost;
+  pd_status ds = build_decode(P, opts, num_cus, (int)P.pf.size(), db_cost);
+  if (ds != PD_OK) return ds;
+  const int n_db = (int)db_cost.size();
 
   // ---- launch order.  Block i is dispatched to XCD i % 8, so blocks are
   // emitted in rounds of 8: a prefill round keeps the XCD affinity of the
@@ -323,10 +439,6 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   // to the price ratio between 100 and 500 flop/B).  block_order 1 runs
   // every prefill tile first and lets the decode blocks fill the CUs that
   // the prefill tail frees.
-  const int n_db = ((int)P.du.size() + pdk::kWavesPerBlock - 1) / pdk::kWavesPerBlock;
-  std::vector<double> db_cost(n_db, 0.0);
-  for (size_t u = 0; u < P.du.size(); ++u)
-    db_cost[u / pdk::kWavesPerBlock] += 2.0 * (P.du[u].k1 - P.du[u].k0) * d.head_dim * elt;
   const int order = opts ? opts->block_order : 0;
   P.block_map.reserve(P.pf.size() + n_db);
   if (order == 1 || P.pf.empty() || n_db == 0) {
@@ -364,15 +476,17 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   off = align_up(off + sizeof(pdk::PrefillItem) * P.pf.size());
   P.off_du = off;
   off = align_up(off + sizeof(pdk::DecodeItem) * P.du.size());
+  P.off_dq = off;
+  off = align_up(off + sizeof(int32_t) * P.dq.size());
   P.off_mg = off;
   off = align_up(off + sizeof(pdk::MergeGroup) * P.mg.size());
   P.off_bmap = off;
   off = align_up(off + sizeof(int32_t) * P.block_map.size());
   P.meta_bytes = off;
   P.off_part_o = off;
-  off = align_up(off + sizeof(float) * (size_t)P.n_parts * pdk::kDecodeCols * d.head_dim);
+  off = align_up(off + sizeof(float) * (size_t)P.n_parts * d.head_dim);
   P.off_part_lse = off;
-  off = align_up(off + sizeof(float) * (size_t)P.n_parts * pdk::kDecodeCols);
+  off = align_up(off + sizeof(float) * (size_t)P.n_parts);
   P.ws_bytes = off;
 
   P.blob.assign(P.meta_bytes, 0);
@@ -384,6 +498,7 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   put(P.off_pages, P.pages.data(), sizeof(int32_t) * P.pages.size());
   put(P.off_pf, P.pf.data(), sizeof(pdk::PrefillItem) * P.pf.size());
   put(P.off_du, P.du.data(), sizeof(pdk::DecodeItem) * P.du.size());
+  put(P.off_dq, P.dq.data(), sizeof(int32_t) * P.dq.size());
   put(P.off_mg, P.mg.data(), sizeof(pdk::MergeGroup) * P.mg.size());
   put(P.off_bmap, P.block_map.data(), sizeof(int32_t) * P.block_map.size());
   return PD_OK;
@@ -441,6 +556,8 @@ pdk::AttnParams attn_params(const pd_plan_s& P, void* d_ws) {
   a.page_indices = (const int32_t*)(ws + P.off_pages);
   a.pf = (const pdk::PrefillItem*)(ws + P.off_pf);
   a.du = (const pdk::DecodeItem*)(ws + P.off_du);
+  a.dq = (const int32_t*)(ws + P.off_dq);
+  a.n_dq = (int32_t)P.dq.size() - 1;
   a.mg = (const pdk::MergeGroup*)(ws + P.off_mg);
   a.block_map = (const int32_t*)(ws + P.off_bmap);
   a.n_blocks = (int32_t)P.block_map.size();
@@ -907,6 +1024,10 @@ int32_t pd_plan_work_items(pd_plan_t plan, int32_t kind, int32_t* out, int32_t m
       width = 4;
       break;
     case 3: src = plan->block_map.data(); count = plan->block_map.size(); width = 1; break;
+    case 4:
+      if (plan->mla) return fail(PD_ERR_INVALID_ARG, "an MLA plan has no decode queues");
+      src = plan->dq.data(); count = plan->dq.size(); width = 1;
+      break;
     default: return fail(PD_ERR_INVALID_ARG, "unknown work item kind");
   }
   if (max_items > 0 && out) {

@@ -29,15 +29,22 @@ __device__ __forceinline__ int64_t page_head_off(const AttnParams& p, int page, 
 }
 
 // ------------------------------------------------------------------------
-// Decode role: one wavefront computes one DecodeItem (<= 16 query rows of
-// one KV head over keys [k0, k1)), 32 keys per step.
+// Decode role: a wavefront runs a queue of DecodeItems (units) one after the
+// other.  A unit is up to 16 NCG query rows of one (request, KV head) over a
+// key range [k0, k1), 32 keys per step:
 //   S^T[key][col] = K Q^T on v_mfma_f32_16x16x32_bf16 (K from HBM straight
-//   into the A operand; Q^T held in registers as the B operand);
+//   into the A operand; Q^T of each 16-row column group held in registers as
+//   the B operand, loaded once per unit);
 //   online softmax per column across the four 16-lane groups;
 //   O^T[d][col] += V^T P^T on the same MFMA, V staged through a per-wave LDS
-//   double buffer by direct global->LDS loads and read back transposed; P^T
-//   comes from the S accumulators without any lane exchange (key order inside
-//   the 32-key step is permuted identically in both operands).
+//   double buffer by direct global->LDS loads and read back transposed (one
+//   read serves every column group); P^T comes from the S accumulators
+//   without any lane exchange (key order inside the 32-key step is permuted
+//   identically in both operands).
+// Every step issues the next step's loads before it computes.  The issue is
+// unconditional: the last step of a unit issues its own loads again (in
+// bounds, never used), so every path through the step loop has the same
+// loads in flight and the compiler's own waits never drain the prefetch.
 // ------------------------------------------------------------------------
 template <int D>
 struct DecodeCfg {
@@ -60,6 +67,8 @@ __device__ __forceinline__ int2 decode_pages(const AttnParams& p, const ReqInfo&
 // Loads of one 32-key step at key b: K fragments into `kf`, V rows into the
 // LDS stage.  Keys >= kv (only in the request's last step) are read from row
 // kv - 1 instead (finite data, masked later), so tail slots are never read.
+// Straight-line code (rows clamped by min, no branch): every path issues the
+// same loads, which keeps the compiler's own wait counts exact.
 template <int D>
 __device__ __forceinline__ void decode_issue(const AttnParams& p, const ReqInfo& ri, int hk, int b, int2 pg,
                                              int lane, u32x4 (&kf)[2][D / 32], LDS_AS char* stage) {
@@ -69,186 +78,204 @@ __device__ __forceinline__ void decode_issue(const AttnParams& p, const ReqInfo&
   const int n = lane & 15, q = lane >> 4;
   const int kvm1 = ri.kv - 1;
   const int r = Lds<D>::dma_row(lane), c = Lds<D>::dma_chunk(lane);
-  if (b + 32 <= ri.kv) {
-    // every row valid: uniform page bases, loop-invariant lane offsets
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int j0 = b + 16 * sb;
-      const int page = sb ? pg.y : pg.x;
-      const int slot0 = j0 & psm;
-      const char* kb = pool + page_head_off(p, page, 0, hk) + slot0 * 2 * D;
-      const char* vb = pool + page_head_off(p, page, 1, hk) + slot0 * 2 * D;
+  for (int sb = 0; sb < 2; ++sb) {
+    const int j0 = b + 16 * sb;
+    const int page = sb ? pg.y : pg.x;
+    const char* kb = pool + page_head_off(p, page, 0, hk);
+    const char* vb = pool + page_head_off(p, page, 1, hk);
+    const int krow = min(j0 + n, kvm1) & psm;
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) kf[sb][ks] = *(const u32x4*)(kb + n * 2 * D + 16 * q + 64 * ks);
+    for (int ks = 0; ks < C::KS; ++ks) kf[sb][ks] = *(const u32x4*)(kb + krow * 2 * D + 16 * q + 64 * ks);
 #pragma unroll
-      for (int i = 0; i < C::VLOADS / 2; ++i)
-        load_lds16_nt(vb + (i * C::RPB + r) * 2 * D + 16 * c,
-                      stage + (sb * (C::VLOADS / 2) + i) * Lds<D>::BLOCK);
-    }
-  } else {
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int j0 = b + 16 * sb;
-      const int page = sb ? pg.y : pg.x;
-      const char* kb = pool + page_head_off(p, page, 0, hk);
-      const char* vb = pool + page_head_off(p, page, 1, hk);
-      const int krow = min(j0 + n, kvm1) & psm;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) kf[sb][ks] = *(const u32x4*)(kb + krow * 2 * D + 16 * q + 64 * ks);
-#pragma unroll
-      for (int i = 0; i < C::VLOADS / 2; ++i) {
-        const int vrow = min(j0 + i * C::RPB + r, kvm1) & psm;
-        load_lds16_nt(vb + vrow * 2 * D + 16 * c, stage + (sb * (C::VLOADS / 2) + i) * Lds<D>::BLOCK);
-      }
+    for (int i = 0; i < C::VLOADS / 2; ++i) {
+      const int vrow = min(j0 + i * C::RPB + r, kvm1) & psm;
+      load_lds16_nt(vb + vrow * 2 * D + 16 * c, stage + (sb * (C::VLOADS / 2) + i) * Lds<D>::BLOCK);
     }
   }
 }
 
+// Per-lane state of a unit: for column group j, this lane's column (lane &
+// 15) is query row c0 + 16 j + (lane & 15) of the row group.
+template <int NCG>
 struct DecodeLanes {
-  int q;         // 16-lane group
-  int v_off;     // lane part of the transposed V read address
+  int q;          // 16-lane group
+  int v_off;      // lane part of the transposed V read address
+  int lim[NCG];   // keys < lim are visible to the lane's column
+  int mask_from;  // smallest lim of any column of the unit (uniform)
 };
 
-// One 32-key step of a decode unit: issue the next step's loads (K into
-// `kn`, V into LDS stage `sn`), wait for this step's, then S, softmax, PV.
-template <int D>
-__device__ __forceinline__ void decode_step(const AttnParams& p, const ReqInfo& ri, int hk, int b, int k1,
-                                            int lim, int mask_from, DecodeLanes ln, int lane,
-                                            const u32x4 (&qf)[D / 32], const u32x4 (&kc)[2][D / 32],
-                                            u32x4 (&kn)[2][D / 32], const LDS_AS char* st, LDS_AS char* sn,
-                                            int2& pg_next, float& m_ref, f32x4& lacc,
-                                            f32x4 (&oacc)[D / 16]) {
+template <int D, int NCG>
+struct DecodeAcc {
+  f32x4 o[NCG][D / 16];
+  f32x4 l[NCG];    // column sums of the bf16 P (all four entries equal)
+  float m[NCG];    // reference maximum of each column
+};
+
+// S, softmax and PV of the 32-key step at key b (K in kc, V in LDS stage st).
+template <int D, int NCG>
+__device__ __forceinline__ void decode_compute(const AttnParams& p, int b, const DecodeLanes<NCG>& ln,
+                                               const u32x4 (&qf)[NCG][D / 32], const u32x4 (&kc)[2][D / 32],
+                                               const LDS_AS char* st, DecodeAcc<D, NCG>& a) {
   using C = DecodeCfg<D>;
   const float cl = p.c_log2;
-  const int nb = b + 32;
-  if (nb < k1) {
-    const int2 pg = pg_next;
-    if (nb + 32 < k1) pg_next = decode_pages(p, ri, nb + 32);  // scalar loads, used next step
-    decode_issue<D>(p, ri, hk, nb, pg, lane, kn, sn);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::KS + C::VLOADS) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  // S^T for keys b + 16 sb + 4 q + i, column lane & 15
-  f32x4 s[2];
+  // S^T for keys b + 16 sb + 4 q + i, column lane & 15 of group j
+  f32x4 s[NCG][2];
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    s[sb] = mfma16(kc[sb][0], qf[0], f32x4{0.f, 0.f, 0.f, 0.f});
+  for (int j = 0; j < NCG; ++j)
 #pragma unroll
-    for (int ks = 1; ks < C::KS; ++ks) s[sb] = mfma16(kc[sb][ks], qf[ks], s[sb]);
-  }
-  if (b + 32 > mask_from) {
+    for (int sb = 0; sb < 2; ++sb) {
+      s[j][sb] = mfma16(kc[sb][0], qf[j][0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (b + 16 * sb + 4 * ln.q + i >= lim) s[sb][i] = -INFINITY;
-  }
-  uint32_t pk[4];
-  {
-    const float mc = m_ref * cl;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        pk[2 * sb + i] = pack_bf16(fast_exp2(__builtin_fmaf(s[sb][2 * i], cl, -mc)),
-                                   fast_exp2(__builtin_fmaf(s[sb][2 * i + 1], cl, -mc)));
-  }
-  if (wave_any(p_out_of_range(pk))) {
-    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mx = max_x16(mx);
-    mx = max_x32(mx);
-    const float m_new = fmaxf(m_ref, mx);
-    if (m_new != -INFINITY) {  // a column with no visible key yet keeps m_ref = -inf
-      const float alpha = fast_exp2((m_ref - m_new) * cl);  // m_ref = -inf -> 0
-      lacc = lacc * alpha;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) oacc[db] = oacc[db] * alpha;
-      m_ref = m_new;
+      for (int ks = 1; ks < C::KS; ++ks) s[j][sb] = mfma16(kc[sb][ks], qf[j][ks], s[j][sb]);
     }
-    const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * cl;
+  if (b + 32 > ln.mask_from) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int j = 0; j < NCG; ++j)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        pk[2 * sb + i] = pack_bf16(fast_exp2(__builtin_fmaf(s[sb][2 * i], cl, -mc)),
-                                   fast_exp2(__builtin_fmaf(s[sb][2 * i + 1], cl, -mc)));
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (b + 16 * sb + 4 * ln.q + i >= ln.lim[j]) s[j][sb][i] = -INFINITY;
   }
-  const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
-  lacc = mfma16(u32x4{kBf16OnesPair, kBf16OnesPair, kBf16OnesPair, kBf16OnesPair}, pb, lacc);
+  u32x4 pb[NCG];
+#pragma unroll
+  for (int j = 0; j < NCG; ++j) {
+    uint32_t pk[4];
+    {
+      const float mc = a.m[j] * cl;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          pk[2 * sb + i] = pack_bf16(fast_exp2(__builtin_fmaf(s[j][sb][2 * i], cl, -mc)),
+                                     fast_exp2(__builtin_fmaf(s[j][sb][2 * i + 1], cl, -mc)));
+    }
+    if (wave_any(p_out_of_range(pk))) {
+      float mx = fmaxf(fmaxf(fmaxf(s[j][0][0], s[j][0][1]), fmaxf(s[j][0][2], s[j][0][3])),
+                       fmaxf(fmaxf(s[j][1][0], s[j][1][1]), fmaxf(s[j][1][2], s[j][1][3])));
+      mx = max_x16(mx);
+      mx = max_x32(mx);
+      const float m_new = fmaxf(a.m[j], mx);
+      if (m_new != -INFINITY) {  // a column with no visible key yet keeps m = -inf
+        const float alpha = fast_exp2((a.m[j] - m_new) * cl);  // m = -inf -> 0
+        a.l[j] = a.l[j] * alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) a.o[j][db] = a.o[j][db] * alpha;
+        a.m[j] = m_new;
+      }
+      const float mc = (a.m[j] == -INFINITY) ? 0.f : a.m[j] * cl;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          pk[2 * sb + i] = pack_bf16(fast_exp2(__builtin_fmaf(s[j][sb][2 * i], cl, -mc)),
+                                     fast_exp2(__builtin_fmaf(s[j][sb][2 * i + 1], cl, -mc)));
+    }
+    pb[j] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    a.l[j] = mfma16(u32x4{kBf16OnesPair, kBf16OnesPair, kBf16OnesPair, kBf16OnesPair}, pb[j], a.l[j]);
+  }
   // V^T[d = 16 db + (lane & 15)][keys 4q + e, 16 + 4q + e]
   const LDS_AS char* vp = st + ln.v_off;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
     const u32x2 a1 = lds_read_tr16(vp + Lds<D>::chunk_step(db));
     const u32x2 a2 = lds_read_tr16(vp + Lds<D>::chunk_step(db) + (16 / C::RPB) * Lds<D>::BLOCK);
-    const u32x4 a = {a1[0], a1[1], a2[0], a2[1]};
-    oacc[db] = mfma16(a, pb, oacc[db]);
+    const u32x4 va = {a1[0], a1[1], a2[0], a2[1]};
+#pragma unroll
+    for (int j = 0; j < NCG; ++j) a.o[j][db] = mfma16(va, pb[j], a.o[j][db]);
   }
 }
 
-template <int D>
-__device__ void decode_unit(const AttnParams& p, int unit, LDS_AS char* lds) {
+// One step of a unit at key b: issue the loads of the next step (this step's
+// again when it is the unit's last: b + 32 >= k1) into kn / sn, wait for this
+// step's, compute it.  Returns false after the unit's last step, with every
+// load landed.
+template <int D, int NCG>
+__device__ __forceinline__ bool decode_step(const AttnParams& p, const ReqInfo& ri, int hk, int k1, int& b,
+                                            int2& pg, int2& pg_next, int lane, const DecodeLanes<NCG>& ln,
+                                            const u32x4 (&qf)[NCG][D / 32], const u32x4 (&kc)[2][D / 32],
+                                            u32x4 (&kn)[2][D / 32], const LDS_AS char* st, LDS_AS char* sn,
+                                            DecodeAcc<D, NCG>& a) {
+  using C = DecodeCfg<D>;
+  const int nb = b + 32;
+  const bool more = nb < k1;
+  decode_issue<D>(p, ri, hk, more ? nb : b, more ? pg_next : pg, lane, kn, sn);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::KS + C::VLOADS) : "memory");
+  const int2 pg_after = decode_pages(p, ri, nb + 32);  // scalar loads, used next step
+  decode_compute<D, NCG>(p, b, ln, qf, kc, st, a);
+  if (!more) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads have landed
+    return false;
+  }
+  b = nb;
+  pg = pg_next;
+  pg_next = pg_after;
+  return true;
+}
+
+// A wavefront's queue: units [u0, u1), each written to its partial rows.
+template <int D, int NCG>
+__device__ void decode_queue(const AttnParams& p, int u0, int u1, LDS_AS char* lds) {
   using C = DecodeCfg<D>;
   const int lane = threadIdx.x & 63;
-  const DecodeItem it = ldc(p.du + unit);
-  const ReqInfo ri = ldc(p.req + it.req);
-  const int g = p.g;
-  const int nrows = ri.qo * g;
   const int n = lane & 15, q = lane >> 4;
-  const bool col_ok = n < nrows;
-  const int t = col_ok ? n / g : 0;
-  const int h = it.hk * g + (col_ok ? n % g : 0);
-  const int lim = min(it.k1, p.causal ? ri.kv - ri.qo + t + 1 : ri.kv);
-  const int mask_from = min(it.k1, p.causal ? ri.kv - ri.qo + 1 : ri.kv);  // smallest lim of any column
-  DecodeLanes ln;
+  const int g = p.g;
+  DecodeLanes<NCG> ln;
   ln.q = q;
-  {
-    const int j = lane & 15;
-    ln.v_off = Lds<D>::off(4 * q + (j >> 2), (j & 3) >> 1) + 8 * (j & 1);
-  }
-
-  u32x4 qf[C::KS];
-  {
-    const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)(ri.qo_start + t) * p.H_q + h) * D + 8 * q;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const u32x4 v = *(const u32x4*)(qp + 32 * ks);
-      qf[ks] = col_ok ? v : u32x4{0, 0, 0, 0};
-    }
-  }
-
-  f32x4 oacc[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;
-  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};  // column sums of the bf16 P (all four entries equal)
-
+  ln.v_off = Lds<D>::off(4 * q + (n >> 2), (n & 3) >> 1) + 8 * (n & 1);
   u32x4 kf0[2][C::KS], kf1[2][C::KS];
   LDS_AS char* st0 = lds;
   LDS_AS char* st1 = lds + C::STAGE_BYTES;
-  int2 pg_next = decode_pages(p, ri, it.k0 + 32);
-  decode_issue<D>(p, ri, it.hk, it.k0, decode_pages(p, ri, it.k0), lane, kf0, st0);
-  for (int b = it.k0;;) {
-    decode_step<D>(p, ri, it.hk, b, it.k1, lim, mask_from, ln, lane, qf, kf0, kf1, st0, st1, pg_next, m_ref,
-                   lacc, oacc);
-    b += 32;
-    if (b >= it.k1) break;
-    decode_step<D>(p, ri, it.hk, b, it.k1, lim, mask_from, ln, lane, qf, kf1, kf0, st1, st0, pg_next, m_ref,
-                   lacc, oacc);
-    b += 32;
-    if (b >= it.k1) break;
-  }
-  const float l_tot = lacc[0];
-  if (col_ok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* po = p.part_o + ((int64_t)it.part * kDecodeCols + n) * D + 4 * q;
+  for (int u = u0; u < u1; ++u) {
+    const DecodeItem it = ldc(p.du + u);
+    const ReqInfo ri = ldc(p.req + it.req);
+    const int rows = ri.qo * g;
+    u32x4 qf[NCG][C::KS];
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) *(f32x4*)(po + 16 * db) = oacc[db] * inv;
-    if (q == 0)
-      p.part_lse[(int64_t)it.part * kDecodeCols + n] =
-          l_tot > 0.f ? m_ref * p.sm_scale + __logf(l_tot) : -INFINITY;
+    for (int j = 0; j < NCG; ++j) {
+      const int row = it.c0 + 16 * j + n;
+      const bool ok = row < rows;
+      const int t = ok ? row / g : 0;
+      const int h = it.hk * g + (ok ? row % g : 0);
+      ln.lim[j] = min(it.k1, p.causal ? ri.kv - ri.qo + t + 1 : ri.kv);
+      const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)(ri.qo_start + t) * p.H_q + h) * D + 8 * q;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const u32x4 v = *(const u32x4*)(qp + 32 * ks);
+        qf[j][ks] = ok ? v : u32x4{0, 0, 0, 0};
+      }
+    }
+    ln.mask_from = min(it.k1, p.causal ? ri.kv - ri.qo + it.c0 / g + 1 : ri.kv);
+    DecodeAcc<D, NCG> a;
+#pragma unroll
+    for (int j = 0; j < NCG; ++j) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) a.o[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      a.l[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      a.m[j] = -INFINITY;
+    }
+    int b = it.k0;
+    int2 pg = decode_pages(p, ri, b);
+    int2 pg_next = decode_pages(p, ri, b + 32);
+    decode_issue<D>(p, ri, it.hk, b, pg, lane, kf0, st0);
+    for (;;) {
+      if (!decode_step<D, NCG>(p, ri, it.hk, it.k1, b, pg, pg_next, lane, ln, qf, kf0, kf1, st0, st1, a)) break;
+      if (!decode_step<D, NCG>(p, ri, it.hk, it.k1, b, pg, pg_next, lane, ln, qf, kf1, kf0, st1, st0, a)) break;
+    }
+    // partial results: row c0 + 16 j + n to partial row part + 16 j + n
+#pragma unroll
+    for (int j = 0; j < NCG; ++j) {
+      if (it.c0 + 16 * j + n < rows) {
+        const float l_tot = a.l[j][0];
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const int64_t pr = (int64_t)it.part + 16 * j + n;
+        float* po = p.part_o + pr * D + 4 * q;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) *(f32x4*)(po + 16 * db) = a.o[j][db] * inv;
+        if (q == 0) p.part_lse[pr] = l_tot > 0.f ? a.m[j] * p.sm_scale + __logf(l_tot) : -INFINITY;
+      }
+    }
   }
 }
 
@@ -604,7 +631,7 @@ __device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
 }
 
 // One launch for both roles: the block map gives each block a prefill tile
-// (v >= 0) or a decode block of eight units, one per wavefront (v < 0).
+// (v >= 0) or a decode block of eight unit queues, one per wavefront (v < 0).
 template <int D>
 constexpr int attn_lds_bytes() {
   return PrefillCfg<D>::LDS_BYTES > kAttnWaves * DecodeCfg<D>::WAVE_LDS ? PrefillCfg<D>::LDS_BYTES
@@ -619,8 +646,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnParams p
     prefill_tile<D>(p, v, lds);
   } else {
     const int w = uniform_i(threadIdx.x >> 6);
-    const int unit = (-v - 1) * kAttnWaves + w;
-    if (unit < p.n_du) decode_unit<D>(p, unit, lds + w * DecodeCfg<D>::WAVE_LDS);
+    const int slot = (-v - 1) * kAttnWaves + w;
+    if (slot < p.n_dq) {
+      const int u0 = ldc(p.dq + slot), u1 = ldc(p.dq + slot + 1);
+      if (u0 < u1) {
+        LDS_AS char* wl = lds + w * DecodeCfg<D>::WAVE_LDS;
+        if (ldc(p.du + u0).ncg == 2)
+          decode_queue<D, 2>(p, u0, u1, wl);
+        else
+          decode_queue<D, 1>(p, u0, u1, wl);
+      }
+    }
   }
 }
 
@@ -708,21 +744,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(AttnParams p) {
       if (lane == 0 && p.lse) p.lse[row] = lse;
     }
   } else {
-    const int unit = (-v - 1) * kWavesPerBlock + w;
-    if (unit >= p.n_du) return;
-    const DecodeItem it = ldc(p.du + unit);
-    const ReqInfo ri = ldc(p.req + it.req);
-    const int nrows = ri.qo * p.g;
-    for (int n = 0; n < nrows; ++n) {
-      const int t = n / p.g, h = it.hk * p.g + n % p.g;
-      const int lim = p.causal ? ri.kv - ri.qo + t + 1 : ri.kv;
-      const int64_t row = (int64_t)(ri.qo_start + t) * p.H_q + h;
-      float o[NO], lse;
-      f32_row<D>(p, ri, it.hk, qbase + row * D, it.k0, min(lim, it.k1), o, lse);
-      float* po = p.part_o + ((int64_t)it.part * kDecodeCols + n) * D;
+    const int slot = (-v - 1) * kWavesPerBlock + w;
+    if (slot >= p.n_dq) return;
+    const int u1 = ldc(p.dq + slot + 1);
+    for (int u = ldc(p.dq + slot); u < u1; ++u) {
+      const DecodeItem it = ldc(p.du + u);
+      const ReqInfo ri = ldc(p.req + it.req);
+      const int nrows = min(ri.qo * p.g, it.c0 + kDecodeCols * it.ncg);
+      for (int n = it.c0; n < nrows; ++n) {
+        const int t = n / p.g, h = it.hk * p.g + n % p.g;
+        const int lim = p.causal ? ri.kv - ri.qo + t + 1 : ri.kv;
+        const int64_t row = (int64_t)(ri.qo_start + t) * p.H_q + h;
+        float o[NO], lse;
+        f32_row<D>(p, ri, it.hk, qbase + row * D, it.k0, min(lim, it.k1), o, lse);
+        const int64_t ps = (int64_t)it.part + (n - it.c0);
+        float* po = p.part_o + ps * D;
 #pragma unroll
-      for (int i = 0; i < NO; ++i) po[lane + 64 * i] = o[i];
-      if (lane == 0) p.part_lse[(int64_t)it.part * kDecodeCols + n] = lse;
+        for (int i = 0; i < NO; ++i) po[lane + 64 * i] = o[i];
+        if (lane == 0) p.part_lse[ps] = lse;
+      }
     }
   }
 }
@@ -741,13 +781,14 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(AttnParams p) {
   for (int idx = threadIdx.x; idx < nrows * D4; idx += kBlockThreads) {
     const int n = idx / D4, d4 = idx % D4;
     const int t = n / p.g, h = mg.hk * p.g + n % p.g;
+    const int64_t base = (int64_t)mg.part0 + n;
+    const int64_t stride = nrows;  // chunk i + 1 is nrows partial rows further
     float mx = -INFINITY;
-    for (int i = 0; i < mg.nparts; ++i)
-      mx = fmaxf(mx, p.part_lse[(int64_t)(mg.part0 + i) * kDecodeCols + n]);
+    for (int i = 0; i < mg.nparts; ++i) mx = fmaxf(mx, p.part_lse[base + i * stride]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float sw = 0.f;
     for (int i = 0; i < mg.nparts; ++i) {
-      const int64_t slot = (int64_t)(mg.part0 + i) * kDecodeCols + n;
+      const int64_t slot = base + i * stride;
       const float li = p.part_lse[slot];
       const float wi = (li == -INFINITY) ? 0.f : __expf(li - mx);
       const f32x4 oi = *(const f32x4*)(p.part_o + slot * D + 4 * d4);

@@ -23,15 +23,19 @@ struct PrefillItem {
   int32_t req, hk, q0, nq, kv_end, rsv0, rsv1, rsv2;
 };
 
-// A split-KV decode unit, computed by one wavefront: all qo * g (<= 16) query
-// rows of (request, KV head) over keys [k0, k1).  Writes a partial result
-// (normalised o and its log-sum-exp) to slot `part`.
+// A split-KV decode unit, computed by one wavefront: query rows [c0, c0 + 16
+// ncg) (clipped to qo * g <= kMaxDecodeRows) of (request, KV head) over keys
+// [k0, k1); row n is token n / g, head hk * g + n % g.  Row c0 + i of the
+// unit writes its partial result (normalised o and its log-sum-exp) to
+// partial row part + i.
 struct DecodeItem {
-  int32_t req, hk, k0, k1, part, rsv0, rsv1, rsv2;
+  int32_t req, hk, k0, k1, part, c0, ncg, rsv;
 };
 
-// The partial results [part0, part0 + nparts) of one (request, KV head) are
-// merged into out / lse by the merge kernel.
+// One (request, KV head) decode row group of rows = qo * g: key chunk i's
+// partial result for row n sits in partial row part0 + i * rows + n; nparts
+// is the number of chunks.  The merge kernel combines the chunks into
+// out / lse.
 struct MergeGroup {
   int32_t req, hk, part0, nparts;
 };
@@ -40,8 +44,9 @@ constexpr int kBlockThreads = 256;  // append, pack, merge and the fp32 kernel
 constexpr int kAttnWaves = 8;       // wavefronts per block of the bf16 attention kernel
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kPrefillRows = 32 * kAttnWaves;  // query rows per prefill tile (32 per wavefront)
-constexpr int kDecodeCols = 16;     // query rows per decode unit (MFMA N)
-constexpr int kWavesPerBlock = kAttnWaves;  // decode units per block (both attention kernels)
+constexpr int kDecodeCols = 16;     // query rows of a decode column group (16x16x32 MFMA N)
+constexpr int kMaxDecodeRows = 64;  // rows of a (request, KV head) the decode role takes
+constexpr int kWavesPerBlock = kAttnWaves;  // decode queues per block (both attention kernels)
 
 struct AttnParams {
   const void* q;
@@ -52,12 +57,14 @@ struct AttnParams {
   const ReqInfo* req;
   const int32_t* page_indices;
   const PrefillItem* pf;
-  const DecodeItem* du;
+  const DecodeItem* du;   // in queue order
+  const int32_t* dq;      // wavefront slot s of the decode blocks runs units [dq[s], dq[s + 1])
   const MergeGroup* mg;
   const int32_t* block_map;  // launch block -> prefill tile (>= 0) or decode block (-b - 1)
-  float* part_o;    // [n_du][kDecodeCols][D]
-  float* part_lse;  // [n_du][kDecodeCols]
+  float* part_o;    // [partial rows][D]
+  float* part_lse;  // [partial rows]
   int32_t n_pf, n_du, n_mg, B;
+  int32_t n_dq;      // decode wavefront slots
   int32_t n_blocks;  // blocks of the attention launch
   int32_t H_q, H_kv, g, ps;
   int32_t ps_shift;  // log2(ps)

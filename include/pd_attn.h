@@ -186,13 +186,19 @@ pd_status pd_plan_get_stats(pd_plan_t plan, pd_plan_stats* out);
 /* Diagnostics: copy the plan's work list (host only).
  *   kind 0: prefill tiles, 8 int32 each:
  *           {request, kv_head, first token, tokens, key end (exclusive), 0,0,0}
- *   kind 1: decode units, 8 int32 each:
- *           {request, kv_head, key begin, key end (exclusive), partial slot,
- *            0,0,0}, four consecutive units per decode block
+ *   kind 1: decode units in queue order, 8 int32 each:
+ *           {request, kv_head, key begin, key end (exclusive), partial row,
+ *            first row c0, 16-row column groups, 0}: rows [c0, c0 + 16 *
+ *           groups) of the (request, KV head)'s qo * g rows; row c0 + i
+ *           writes partial row + i
  *   kind 2: merge groups, 4 int32 each:
- *           {request, kv_head, first partial slot, partial count}
+ *           {request, kv_head, first partial row, chunk count}; chunk i's
+ *           result for row n is partial row first + i * qo g + n
  *   kind 3: the attention launch's blocks in launch order, 1 int32 each:
  *           v >= 0 is prefill tile v, v < 0 is decode block -v - 1
+ *   kind 4: decode queue offsets, 1 int32 each (wavefront slots + 1
+ *           entries): wavefront w of decode block b runs the units
+ *           [q[8 b + w], q[8 b + w + 1]) of kind 1, one after the other
  * Writes at most max_items items to out (which may be NULL when max_items is
  * 0) and returns the total number of items of that kind, or a negative
  * pd_status (PD_ERR_INVALID_ARG for a NULL plan or an unknown kind). */

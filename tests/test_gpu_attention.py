@@ -10,7 +10,9 @@ N(0,1) data, about 3e-4 where logits reach 300 nats).  Cases span the
 five seeded workloads (the long one at reduced length here; full length in
 test_gpu_long), several tiles and ragged tails, every supported head_dim,
 page size and GQA group, causal and non-causal, qo = 0 requests, the
-decode/prefill boundary (qo * g = 16 / 17), and a sharpened softmax."""
+decode unit widths (qo * g = 16 / 17, 32 / 33, 64 / 65: one 16-row column
+group, two, two wavefronts of two, then prefill tiles), and a sharpened
+softmax."""
 import functools
 
 import numpy as np
@@ -67,6 +69,15 @@ RAGGED = [
     ("prefill", ((513, 1), (1000, 1)), dict(heads=(8, 8))),
     ("long", ((1000, 1, 1), (3000, 3000, 64)), dict(heads=(64, 8))),    # long at reduced size
     ("long", ((48, 2), (96, 4100)), dict(heads=(128, 1), page_size=16)),  # g = 128
+    # wide decode row groups (qo * g of 17 .. 64 rows: 32-row units, and two
+    # 32-row units per chunk side by side above 32 rows) over long caches
+    ("long", ((1, 1, 1), (16500, 700, 33)), dict(heads=(256, 8))),       # g = 32
+    ("long", ((1, 1), (17000, 900)), dict(heads=(64, 1))),               # g = 64
+    ("long", ((4, 4, 1, 2), (16400, 500, 3000, 90)), dict(heads=(64, 8))),  # qo = 4 at g = 8
+    ("mixed", ((1, 3, 8, 1, 9), (2500, 4100, 300, 60, 700)), dict(heads=(64, 8))),  # 8/24/64/8/72 rows
+    ("mixed", ((1, 1, 2), (3000, 70, 1500)), dict(heads=(33, 1))),         # 33 / 33 / 66 rows
+    ("mixed", ((1, 3, 2), (1800, 2000, 45)), dict(heads=(48, 3))),         # 16 / 48 / 32 rows
+    ("tiny", ((5, 9, 2), (40, 300, 17)), dict(heads=(28, 4))),             # fp32: 35 / 63 / 14 rows
 ]
 
 
@@ -102,6 +113,8 @@ def test_rising_logits(nats):
     check(rising_logits(make_batch("mixed", lengths=((300, 1, 2), (300, 2000, 900)), heads=(16, 4)), nats),
           f"rising{nats}")
     check(rising_logits(make_batch("tiny", lengths=((40, 1), (100, 300))), nats), f"rising{nats}_f32")
+    check(rising_logits(make_batch("mixed", lengths=((1, 1, 3), (2000, 333, 900)), heads=(64, 2)), nats),
+          f"rising{nats}_wide")
 
 
 def test_sharpened_softmax():
@@ -112,10 +125,38 @@ def test_sharpened_softmax():
 
 @pytest.mark.parametrize("chunk", [32, 96, 512])
 def test_split_count_invariance(chunk):
-    b = batch("mixed", ((1, 2, 1, 3), (4000, 3000, 2048, 700)))
-    out0, _ = DeviceRun(b).step()
-    out1, _ = check(b, f"split{chunk}", chunk=chunk)
-    assert np.abs(out1 - out0).max() <= 2 * tolerance(b)
+    for heads in ((32, 8), (64, 2)):   # 16-row and 32/64-row decode units
+        b = batch("mixed", ((1, 2, 1, 3), (4000, 3000, 2048, 700)), heads=heads)
+        out0, _ = DeviceRun(b).step()
+        out1, _ = check(b, f"split{chunk}_{heads}", chunk=chunk)
+        assert np.abs(out1 - out0).max() <= 2 * tolerance(b)
+
+
+QUEUE_CASES = [
+    # (workload, lengths, overrides, planner CUs, chunk): few CUs give every
+    # wavefront a long span of keys crossing many row groups (requests,
+    # heads, unit kinds), so its queue holds many units
+    ("mixed", ((1, 2, 1, 3, 1, 0, 1), (4000, 3000, 2048, 700, 1, 5, 33)), {}, 1, 0),
+    ("mixed", ((1, 3, 8, 1, 2), (2500, 4100, 300, 60, 900)), dict(heads=(64, 8)), 2, 0),
+    ("mixed", ((1, 1, 1, 1), (3000, 95, 1500, 40)), dict(heads=(64, 1)), 1, 0),
+    ("decode", None, {}, 4, 0),
+    ("tiny", ((5, 9, 2, 1), (40, 300, 17, 100)), dict(heads=(28, 4)), 1, 0),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(QUEUE_CASES)))
+def test_decode_queues_of_many_units(idx):
+    wid, lengths, kw, cus, chunk = QUEUE_CASES[idx]
+    b = batch(wid, lengths, **kw)
+    run = DeviceRun(b, decode_chunk_keys=chunk, num_cus=cus)
+    dq = run.plan.work_items(4)[:, 0]
+    assert np.diff(dq).max() >= 3, "the case should queue several units per wavefront"
+    print(f"case queues{idx}: {len(dq) - 1} queues, up to {np.diff(dq).max()} units each", flush=True)
+    out, lse = run.step()
+    O, L = oracle_outputs(b)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    assert report(f"queues{idx}", out, O) <= tolerance(b)
+    assert np.abs(lse - L).max() <= lse_tol(b) + 2.0 ** -20 * np.abs(L).max()
 
 
 def test_bitwise_deterministic_for_a_fixed_plan():

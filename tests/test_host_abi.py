@@ -210,35 +210,78 @@ def test_pack_bytes_formula():
 
 
 # ------------------------------------------------------------- planner cover
+MAX_DECODE_ROWS = 64   # rows of a (request, KV head) that the decode role takes
+
+
 def check_cover(b, plan):
-    """Every (request, query head, row) is computed exactly once, prefill
-    tiles see exactly their causal key range, decode chunks tile [0, kv)."""
+    """Every (request, query head, row) is computed exactly once: prefill
+    tiles see exactly their causal key range; a decode row group's chunks
+    tile [0, kv), every chunk's units cover the group's rows once, each unit
+    writes the partial slots the merge group reads; the queues hold every
+    unit once, each queue one kind of unit, and the two halves of a 64-row
+    group's chunk sit in adjacent wavefronts of one block."""
     g = b.H_q // b.H_kv
-    pf, du, mg = plan.work_items(0), plan.work_items(1), plan.work_items(2)
+    pf, du, mg, dq = plan.work_items(0), plan.work_items(1), plan.work_items(2), plan.work_items(4)[:, 0]
     seen = {}
     for (r, hk, q0, nq, kv_end, *_rest) in pf:
         qo, kv = int(b.qo_lens[r]), int(b.kv_lens[r])
-        assert qo * g > 16
+        assert qo * g > MAX_DECODE_ROWS
         assert nq * g <= 256 and 0 <= q0 and q0 + nq <= qo
         assert kv_end == (kv - qo + q0 + nq if b.causal else kv)
         for t in range(q0, q0 + nq):
             for h in range(hk * g, hk * g + g):
                 seen[(r, h, t)] = seen.get((r, h, t), 0) + 1
-    parts = {}
-    for (r, hk, k0, k1, part, *_rest) in du:
-        assert k0 % 32 == 0 and k0 < k1 <= int(b.kv_lens[r])
-        parts[part] = (r, hk, k0, k1)
-    assert sorted(parts) == list(range(len(du)))
-    for (r, hk, p0, n) in mg:
+    # queues
+    assert dq[0] == 0 and dq[-1] == len(du) and (np.diff(dq) >= 0).all()
+    for s in range(len(dq) - 1):
+        q = du[dq[s]:dq[s + 1]]
+        if len(q):
+            assert len(set(q[:, 6].tolist())) == 1, "a queue mixes unit kinds"
+    slot_of_unit = np.repeat(np.arange(len(dq) - 1), np.diff(dq))
+    pos_in_queue = np.concatenate([np.arange(n) for n in np.diff(dq)]) if len(du) else np.zeros(0, int)
+    units = {}
+    used_slots = set()
+    first_half = {(r, hk, k0, k1): i for i, (r, hk, k0, k1, _p, c0, _n, _z) in enumerate(du.tolist()) if c0 == 0}
+    for i, (r, hk, k0, k1, part, c0, ncg, _z) in enumerate(du.tolist()):
         qo, kv = int(b.qo_lens[r]), int(b.kv_lens[r])
-        assert qo * g <= 16
-        chunks = sorted(parts[p][2:] for p in range(p0, p0 + n))
-        assert all(parts[p][:2] == (r, hk) for p in range(p0, p0 + n))
+        rows = qo * g
+        assert 1 <= rows <= MAX_DECODE_ROWS
+        assert k0 % 32 == 0 and 0 <= k0 < k1 <= kv
+        assert ncg == (1 if rows <= 16 else 2) and c0 % 32 == 0 and c0 < rows
+        units.setdefault((r, hk), []).append((k0, k1, part, c0, ncg, i))
+        for n in range(c0, min(rows, c0 + 16 * ncg)):
+            assert part + n - c0 not in used_slots
+            used_slots.add(part + n - c0)
+        if c0 == 32:   # the second half of a 64-row group's chunk: next wavefront, same block, same position
+            t = first_half[(r, hk, k0, k1)]
+            assert slot_of_unit[i] == slot_of_unit[t] + 1 and slot_of_unit[t] % 2 == 0
+            assert pos_in_queue[i] == pos_in_queue[t]
+    groups = {}
+    for (r, hk, p0, n) in mg.tolist():
+        assert (r, hk) not in groups
+        groups[(r, hk)] = (p0, n)
+    assert set(groups) == set(units)
+    for (r, hk), us in units.items():
+        qo, kv = int(b.qo_lens[r]), int(b.kv_lens[r])
+        rows = qo * g
+        p0, n = groups[(r, hk)]
+        chunks = sorted({(k0, k1) for k0, k1, *_ in us})
+        assert len(chunks) == n
         assert chunks[0][0] == 0 and chunks[-1][1] == kv
         assert all(chunks[i][1] == chunks[i + 1][0] for i in range(n - 1))
+        for ci, (k0, k1) in enumerate(chunks):
+            covered = []
+            for (a0, a1, part, c0, ncg, _i) in us:
+                if (a0, a1) != (k0, k1):
+                    continue
+                assert part == p0 + ci * rows + c0
+                covered += list(range(c0, min(rows, c0 + 16 * ncg)))
+            assert sorted(covered) == list(range(rows))
         for t in range(qo):
             for h in range(hk * g, hk * g + g):
                 seen[(r, h, t)] = seen.get((r, h, t), 0) + 1
+    n_rows = sum(n * int(b.qo_lens[r]) * g for (r, hk), (p0, n) in groups.items())
+    assert used_slots == set(range(n_rows))
     expect_keys = {(r, h, t) for r in range(b.B) for h in range(b.H_q) for t in range(int(b.qo_lens[r]))}
     assert set(seen) == expect_keys
     assert all(v == 1 for v in seen.values())
@@ -254,13 +297,18 @@ def check_cover(b, plan):
     ("tiny", dict(lengths=([4, 16, 1], [4, 40, 1]), heads=(8, 2))),
     ("tiny", dict(lengths=([33, 3], [33, 70]), causal=False)),
     ("long", dict(lengths=([1, 3, 9], [5000, 64, 9]), heads=(24, 8))),
+    ("long", dict(lengths=([1, 1, 2, 4, 8, 9, 1], [20000, 33, 700, 4000, 64, 900, 17000]), heads=(64, 8))),
+    ("long", dict(lengths=([1, 1, 1], [17000, 40, 1200]), heads=(64, 1))),
+    ("long", dict(lengths=([1, 1, 2], [17000, 40, 1200]), heads=(32, 1))),
+    ("mixed", dict(lengths=([1, 300, 1, 4, 1], [5000, 800, 70, 3000, 1]), heads=(32, 2))),
 ])
 def test_planner_covers_batch(wid, kw):
     b = make_batch(wid, materialize=False, **kw)
     d = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype, b.causal)
     plan = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages)
     check_cover(b, plan)
-    for chunk in (32, 100, 4096):
+    big = int(b.kv_lens.astype(np.int64).sum()) > 1_000_000   # keep the per-unit Python check small
+    for chunk in ((2048, 4096) if big else (32, 100, 4096)):
         plan = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages,
                           decode_chunk_keys=chunk)
         check_cover(b, plan)
@@ -268,12 +316,17 @@ def test_planner_covers_batch(wid, kw):
 
 def test_planner_work_figures_match_closed_forms():
     """prefill flops = 4 D H_q x visible pairs; decode bytes = K + V read."""
-    for wid, flops, dbytes in [("tiny", 713_728, 40_960), ("prefill", 21_516_779_520, 0)]:
+    # the tiny workload's 713,728 algorithmic prefill flops (pairs 136 + 561):
+    assert 4 * 64 * 4 * (16 * 17 // 2 + 33 * 34 // 2) == 713_728
+    # its 16-token request has 32 rows (g = 2), few enough for the decode role;
+    # the plan counts the flops of the rows it gives to prefill tiles
+    for wid, flops, dbytes in [("tiny", 4 * 64 * 4 * 561, (16 + 40) * 2 * 2 * 64 * 4),
+                               ("prefill", 21_516_779_520, 0)]:
         b = make_batch(wid, materialize=False)
         d = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype)
         s = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages).stats()
         pairs = sum(q * (k - q) + q * (q + 1) // 2 for q, k in zip(b.qo_lens.tolist(), b.kv_lens.tolist())
-                    if q * (b.H_q // b.H_kv) > 16)
+                    if q * (b.H_q // b.H_kv) > MAX_DECODE_ROWS)
         assert s.prefill_flops == 4 * b.D * b.H_q * pairs
         assert s.prefill_flops == flops and s.decode_kv_bytes == dbytes
     b = make_batch("long", materialize=False)
@@ -292,8 +345,8 @@ def test_block_map_covers_work_and_keeps_xcd_affinity(order):
     d = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype)
     plan = pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages,
                       block_order=order)
-    pf, du, bmap = plan.work_items(0), plan.work_items(1), plan.work_items(3)[:, 0]
-    n_db = (len(du) + 7) // 8   # eight decode units (one per wavefront) per block
+    pf, dq, bmap = plan.work_items(0), plan.work_items(4), plan.work_items(3)[:, 0]
+    n_db = (len(dq) - 1 + 7) // 8   # eight decode queues (one per wavefront) per block
     assert sorted(bmap[bmap >= 0].tolist()) == list(range(len(pf)))
     assert sorted((-bmap[bmap < 0] - 1).tolist()) == list(range(n_db))
     xcd_of_head = {}
