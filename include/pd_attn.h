@@ -87,9 +87,7 @@ typedef enum pd_dtype { PD_F32 = 0, PD_BF16 = 1 } pd_dtype;
 
 /* Shape of one attention layer.
  *   num_qo_heads  query heads H_q (> 0, multiple of num_kv_heads)
- *   num_kv_heads  KV heads H_kv (> 0); g = H_q / H_kv <= 256; g <= 16 for
- *                 single-token (decode) rows, larger groups are supported
- *                 for prefill rows only
+ *   num_kv_heads  KV heads H_kv (> 0); g = H_q / H_kv <= 256
  *   head_dim      64 or 128
  *   page_size     16, 32, 64 or 128 tokens per page
  *   dtype         pd_dtype of pool, q, k_new, v_new
@@ -106,8 +104,15 @@ typedef struct pd_attn_desc {
 } pd_attn_desc;
 
 /* Optional planner controls (NULL = defaults).
- *   decode_chunk_keys  keys per split-KV chunk of a decode row group; 0 lets
- *                      the planner choose; otherwise rounded up to 32
+ *   decode_chunk_keys  0 (default): when the launch has fewer prefill tiles
+ *                      than compute units, the decode row groups are laid
+ *                      end to end and cut into equal spans of keys, one per
+ *                      wavefront queue (a queue holds the units its span
+ *                      crosses); otherwise each group is cut into equal
+ *                      chunks of a length the planner picks, one unit each.
+ *                      > 0: every group is cut into chunks of about this
+ *                      many keys (rounded up to 32, at most the longest
+ *                      cache), one unit per queue
  *   num_cus            compute units to balance over; 0 = 256 (MI355X)
  *   block_order        order of the blocks of the attention launch:
  *                      0 = interleave prefill and decode rounds by their
@@ -127,9 +132,10 @@ typedef struct pd_plan_stats {
   int32_t batch;
   int32_t total_q_rows;        /* sum qo */
   int32_t prefill_tiles;       /* MFMA query tiles (rows of prefill requests) */
-  int32_t decode_units;        /* split-KV units (one wavefront each) */
+  int32_t decode_units;        /* split-KV units */
   int32_t decode_row_groups;   /* (request, kv head) groups merged */
-  int32_t decode_chunk_keys;   /* chunk length used */
+  int32_t decode_chunk_keys;   /* chunk length used (span planning: the
+                                  longest unit) */
   int64_t prefill_flops;       /* 4 * head_dim * H_q * visible (query, key)
                                   pairs of the prefill rows (algorithmic) */
   int64_t decode_kv_bytes;     /* K + V bytes the decode rows read */
@@ -155,8 +161,13 @@ typedef struct pd_plan_s* pd_plan_t;
  * performance"): each step batches prefill requests (many query tokens,
  * compute bound) with decode requests (qo_len = 1, bound by reading the
  * kv_len-long cache), and attention is spread over both the requests and
- * their kv_len to keep the device busy.  Rows of requests with qo * g <= 16
- * become split-KV decode units; the rest become causal MFMA query tiles.
+ * their kv_len to keep the device busy.  A request whose qo * g query rows
+ * per KV head number at most 64 (single-token decode at g <= 64, or a
+ * multi-token step such as 4 tokens at g = 8) is split over its kv_len into
+ * decode units of 16 or 32 rows, one wavefront each (two side by side on the
+ * same keys above 32 rows), whose partial results are merged afterwards; the
+ * rows of every other request become causal MFMA query tiles of up to 256
+ * rows, each over its whole causal key range.
  * Errors: PD_ERR_INVALID_ARG (null pointers, batch < 1, negative lengths,
  * qo > kv, wrong page count, duplicate page id, H_q % H_kv != 0),
  * PD_ERR_OUT_OF_RANGE (page id outside the pool), PD_ERR_UNSUPPORTED
