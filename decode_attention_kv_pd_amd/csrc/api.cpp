@@ -102,6 +102,7 @@ struct pd_plan_s {
   std::vector<pdk::MergeGroup> mg;
   std::vector<int32_t> block_map;  // attention launch order
   size_t off_qo = 0, off_req = 0, off_pages = 0, off_pf = 0, off_du = 0, off_dq = 0, off_mg = 0, off_bmap = 0;
+  size_t off_rows = 0;  // (page, slot) of each new row, for the append
   size_t meta_bytes = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   int64_t prefill_flops = 0, decode_bytes = 0;
   std::vector<char> blob;  // host image of the workspace tables
@@ -482,6 +483,8 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   off = align_up(off + sizeof(pdk::MergeGroup) * P.mg.size());
   P.off_bmap = off;
   off = align_up(off + sizeof(int32_t) * P.block_map.size());
+  P.off_rows = off;
+  off = align_up(off + sizeof(int32_t) * 2 * (size_t)P.total_rows);
   P.meta_bytes = off;
   P.off_part_o = off;
   off = align_up(off + sizeof(float) * (size_t)P.n_parts * d.head_dim);
@@ -501,6 +504,17 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   put(P.off_dq, P.dq.data(), sizeof(int32_t) * P.dq.size());
   put(P.off_mg, P.mg.data(), sizeof(pdk::MergeGroup) * P.mg.size());
   put(P.off_bmap, P.block_map.data(), sizeof(int32_t) * P.block_map.size());
+  {
+    int32_t* rp = (int32_t*)(P.blob.data() + P.off_rows);
+    for (int r = 0; r < P.B; ++r) {
+      const pdk::ReqInfo& ri = P.req[r];
+      for (int i = 0; i < ri.qo; ++i) {
+        const int pos = ri.kv - ri.qo + i;
+        rp[2 * (ri.qo_start + i)] = P.pages[ri.page_start + pos / d.page_size];
+        rp[2 * (ri.qo_start + i) + 1] = pos % d.page_size;
+      }
+    }
+  }
   return PD_OK;
 }
 
@@ -908,15 +922,14 @@ pd_status enqueue_append(pd_plan_t plan, void* d_ws, void* kv_pool, const void* 
   p.pool = kv_pool;
   p.k_new = k_new;
   p.v_new = v_new;
-  p.qo_indptr = (const int32_t*)(ws + plan->off_qo);
-  p.req = (const pdk::ReqInfo*)(ws + plan->off_req);
-  p.page_indices = (const int32_t*)(ws + plan->off_pages);
-  p.B = plan->B;
+  p.rowpos = (const int2*)(ws + plan->off_rows);
   p.total_rows = plan->total_rows;
   p.H_kv = plan->desc.num_kv_heads;
   p.ps = plan->desc.page_size;
   p.D = plan->desc.head_dim;
   p.elt = elt_bytes(&plan->desc);
+  const int row_bytes = 2 * p.H_kv * p.D * p.elt;
+  p.rows_per_block = std::max(1, 16384 / row_bytes);  // about 16 KB per block
   hipError_t e = pdk::launch_append(p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   return PD_OK;

@@ -38,32 +38,41 @@ __device__ __forceinline__ T ldc(const T* p) {
 }
 
 // ------------------------------------------------------------------------
-// KV append: one block per new token row; 16-byte copies of each head's K
-// and V row into (page, slot) of position kv - qo + i.
+// KV append: the new rows are cut into 16-byte chunks (a row is 2 H_kv heads
+// of D elements, K then V); a block copies `rows_per_block` consecutive rows
+// (about 16 KB), each thread four chunks at a time (loads, then stores).  The
+// (page, slot) of every row comes from the planner's row table.
 // ------------------------------------------------------------------------
+constexpr int kAppendBatch = 4;
+
 __global__ __launch_bounds__(kBlockThreads) void append_kernel(AppendParams p) {
-  const int row = blockIdx.x;
-  int lo = 0, hi = p.B - 1;  // last request with qo_indptr[r] <= row
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (ldc(p.qo_indptr + mid) <= row) lo = mid; else hi = mid - 1;
-  }
-  const ReqInfo ri = ldc(p.req + lo);
-  const int pos = ri.kv - ri.qo + (row - ri.qo_start);
-  const int page = ldc(p.page_indices + ri.page_start + pos / p.ps);
-  const int slot = pos % p.ps;
-  const int64_t head_bytes = (int64_t)p.D * p.elt;
-  const int cph = (int)(head_bytes / 16);
-  const int64_t page_bytes = 2 * (int64_t)p.H_kv * p.ps * head_bytes;
-  char* pool = (char*)p.pool + (int64_t)page * page_bytes;
-  const int total = 2 * p.H_kv * cph;
-  for (int c = threadIdx.x; c < total; c += kBlockThreads) {
-    const int kvsel = c / (p.H_kv * cph);
-    const int hh = (c / cph) % p.H_kv;
-    const int cc = c % cph;
-    const char* src = (const char*)(kvsel ? p.v_new : p.k_new) + ((int64_t)row * p.H_kv + hh) * head_bytes + cc * 16;
-    char* dst = pool + (((int64_t)kvsel * p.H_kv + hh) * p.ps + slot) * head_bytes + cc * 16;
-    *(u32x4*)dst = *(const u32x4*)src;
+  const int cph = p.D * p.elt / 16;             // chunks per head row
+  const int cpr = 2 * p.H_kv * cph;             // chunks per token row
+  const int row0 = blockIdx.x * p.rows_per_block;
+  const int nrows = min(p.rows_per_block, p.total_rows - row0);
+  const int nchunks = nrows * cpr;
+  const int64_t page_bytes = (int64_t)cpr * 16 * p.ps;
+  for (int c0 = threadIdx.x; c0 < nchunks; c0 += kBlockThreads * kAppendBatch) {
+    u32x4 v[kAppendBatch];
+    char* dst[kAppendBatch];
+#pragma unroll
+    for (int k = 0; k < kAppendBatch; ++k) {
+      const int c = c0 + k * kBlockThreads;
+      dst[k] = nullptr;
+      if (c < nchunks) {
+        const int r = c / cpr, rem = c - r * cpr;
+        const int kvsel = rem / (p.H_kv * cph), hc = rem - kvsel * (p.H_kv * cph);  // head * cph + part
+        const int row = row0 + r;
+        const int2 at = p.rowpos[row];                                                // (page, slot)
+        const char* src = (const char*)(kvsel ? p.v_new : p.k_new) + ((int64_t)row * p.H_kv * cph + hc) * 16;
+        const int hh = hc / cph, part = hc - hh * cph;
+        dst[k] = (char*)p.pool + at.x * page_bytes + ((int64_t)((kvsel * p.H_kv + hh) * p.ps + at.y) * cph + part) * 16;
+        v[k] = *(const u32x4*)src;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kAppendBatch; ++k)
+      if (dst[k]) *(u32x4*)dst[k] = v[k];
   }
 }
 
@@ -155,7 +164,8 @@ __global__ __launch_bounds__(kBlockThreads) void xfer_kernel(XferParams p) {
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s) {
   if (p.total_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(append_kernel, dim3(p.total_rows), dim3(kBlockThreads), 0, s, p);
+  const unsigned blocks = (unsigned)((p.total_rows + p.rows_per_block - 1) / p.rows_per_block);
+  hipLaunchKernelGGL(append_kernel, dim3(blocks), dim3(kBlockThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -78,10 +78,9 @@ struct AppendParams {
   void* pool;
   const void* k_new;
   const void* v_new;
-  const int32_t* qo_indptr;  // [B + 1]
-  const ReqInfo* req;
-  const int32_t* page_indices;
-  int32_t B, total_rows, H_kv, ps, D, elt;
+  const int2* rowpos;        // [total_rows]: (page id, slot) of each new row
+  int32_t total_rows, H_kv, ps, D, elt;
+  int32_t rows_per_block;
 };
 
 // Page transfers between a pool (or L layer pools) and a buffer

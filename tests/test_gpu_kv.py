@@ -29,6 +29,7 @@ CASES = [
     ("mixed", ((1, 5, 2, 300, 0, 17, 64), (1, 100, 64, 300, 9, 1000, 64)), {}),
     ("long", ((3, 1, 70), (3, 200, 130)), dict(page_size=128)),
     ("tiny", ((7, 1), (50, 33)), dict(page_size=32, head_dim=128)),
+    ("tiny", ((3, 2, 5, 0, 11), (10, 40, 70, 3, 11)), dict(heads=(12, 3))),   # 96 chunks per row
 ]
 
 
