@@ -117,6 +117,29 @@ def test_rising_logits(nats):
           f"rising{nats}_wide")
 
 
+@pytest.mark.parametrize("log2_scale,nats", [(20, 1.0), (40, 0.6)])
+def test_large_values_scale_exactly(log2_scale, nats):
+    """V times 2^k (exact in bf16) under rising logits: every output row is
+    the unscaled run's times 2^k bit for bit and the LSE is unchanged.  At
+    0.6 nat per key a 64-key tile raises the logits by about 38 nats, below
+    the speculative softmax's rescale trigger (weights of 2^64), so weights
+    up to about 2^55 multiply values up to 2^44 in the fp32 accumulators; the
+    exact scaling shows that nothing overflows or rounds differently.  The
+    scaled-back rows meet the usual bar against the oracle."""
+    def make():
+        return rising_logits(make_batch("mixed", lengths=((300, 1, 2), (300, 2000, 900)), heads=(16, 4)), nats)
+    base, big = make(), make()
+    big.v = f32_to_bf16_bits(bf16_bits_to_f32(big.v) * np.float32(2.0 ** log2_scale))
+    assert np.array_equal(bf16_bits_to_f32(big.v), bf16_bits_to_f32(base.v) * np.float32(2.0 ** log2_scale))
+    out0, lse0 = DeviceRun(base).step()
+    out1, lse1 = DeviceRun(big).step()
+    assert np.isfinite(out1).all()
+    assert np.array_equal(out1, out0 * np.float32(2.0 ** log2_scale))
+    assert np.array_equal(lse1.view(np.uint32), lse0.view(np.uint32))
+    O, _ = oracle_outputs(base)
+    assert report(f"large{log2_scale}", out1 / np.float32(2.0 ** log2_scale), O) <= tolerance(base)
+
+
 def test_sharpened_softmax():
     """Q scaled by 8: logits of order 8, far from uniform weights."""
     check(batch("mixed", ((200, 1, 1), (260, 900, 33)), q_gain=8.0), "sharp")

@@ -2,9 +2,10 @@
 cached tokens plus 256 single-token decodes over 32768 cached tokens; 64/8
 heads, head_dim 128, bf16, page size 64), in the launch configuration the
 benchmark times (default plan).  The pool (about 36 GB) is drawn on the
-device; sampled output rows are checked one by one against the oracle, the
-sampled requests' pages are checked bit-exactly after the append, and the
-chunk request's 512 pages go through pack and unpack."""
+device; sampled output rows (33 decode requests, about 75 chunk tokens at
+32-token tile edges) are checked one by one against the oracle, the sampled
+requests' pages are checked bit-exactly after the append, and the chunk
+request's 512 pages go through pack and unpack."""
 import numpy as np
 import pytest
 import torch
@@ -16,8 +17,13 @@ from workloads import device_normal_, device_seed, make_batch
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE_REQUESTS = (0, 1, 97, 256)
-PREFILL_TOKENS = (0, 1, 2, 63, 64, 127, 4095, 4096, 8190, 8191)
+# the chunk request and 33 of the 256 decode requests, spread over the launch
+# (their units land in blocks of every XCD and both key chunks)
+SAMPLE_REQUESTS = (0,) + tuple(range(1, 257, 8)) + (256,)
+# chunk tokens at the edges of its 32-token tiles (every eighth tile), at the
+# start, the middle and the end
+PREFILL_TOKENS = tuple(sorted({0, 1, 2, 63, 64, 127, 4095, 4096, 8190, 8191} |
+                              {e for k in range(1, 256, 8) for e in (32 * k - 1, 32 * k)}))
 
 
 def pages_host(pool, ids):
