@@ -65,10 +65,10 @@ __device__ __forceinline__ int2 decode_pages(const AttnParams& p, const ReqInfo&
 }
 
 // Loads of one 32-key step at key b: K fragments into `kf`, V rows into the
-// LDS stage.  Keys >= kv (only in the request's last step) are read from row
-// kv - 1 instead (finite data, masked later), so tail slots are never read.
-// Straight-line code (rows clamped by min, no branch): every path issues the
-// same loads, which keeps the compiler's own wait counts exact.
+// LDS stage, all from inline asm (2 KS + VLOADS loads, in this order), so
+// the step loop alone decides how long to wait for them.  Keys >= kv (only
+// in the request's last step) are read from row kv - 1 instead (finite data,
+// masked later), so tail slots are never read.
 template <int D>
 __device__ __forceinline__ void decode_issue(const AttnParams& p, const ReqInfo& ri, int hk, int b, int2 pg,
                                              int lane, u32x4 (&kf)[2][D / 32], LDS_AS char* stage) {
@@ -85,8 +85,7 @@ __device__ __forceinline__ void decode_issue(const AttnParams& p, const ReqInfo&
     const char* kb = pool + page_head_off(p, page, 0, hk);
     const char* vb = pool + page_head_off(p, page, 1, hk);
     const int krow = min(j0 + n, kvm1) & psm;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) kf[sb][ks] = *(const u32x4*)(kb + krow * 2 * D + 16 * q + 64 * ks);
+    load_frags64<C::KS>(kb + krow * 2 * D + 16 * q, kf[sb]);
 #pragma unroll
     for (int i = 0; i < C::VLOADS / 2; ++i) {
       const int vrow = min(j0 + i * C::RPB + r, kvm1) & psm;
@@ -194,18 +193,28 @@ __device__ __forceinline__ void decode_compute(const AttnParams& p, int b, const
 template <int D, int NCG>
 __device__ __forceinline__ bool decode_step(const AttnParams& p, const ReqInfo& ri, int hk, int k1, int& b,
                                             int2& pg, int2& pg_next, int lane, const DecodeLanes<NCG>& ln,
-                                            const u32x4 (&qf)[NCG][D / 32], const u32x4 (&kc)[2][D / 32],
+                                            u32x4 (&qf)[NCG][D / 32], u32x4 (&kc)[2][D / 32],
                                             u32x4 (&kn)[2][D / 32], const LDS_AS char* st, LDS_AS char* sn,
                                             DecodeAcc<D, NCG>& a) {
   using C = DecodeCfg<D>;
   const int nb = b + 32;
   const bool more = nb < k1;
   decode_issue<D>(p, ri, hk, more ? nb : b, more ? pg_next : pg, lane, kn, sn);
+  // this step's K and V (and the unit's Q, loaded before its first step)
+  // have landed; the next step's loads stay in flight through the compute
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::KS + C::VLOADS) : "memory");
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) pin_regs(kc[sb]);
+#pragma unroll
+  for (int j = 0; j < NCG; ++j) pin_regs(qf[j]);
   const int2 pg_after = decode_pages(p, ri, nb + 32);  // scalar loads, used next step
   decode_compute<D, NCG>(p, b, ln, qf, kc, st, a);
   if (!more) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads have landed
+    // the repeated loads have landed; kn stays live up to here, so that the
+    // compiler places nothing else in its registers while they are in flight
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) pin_regs(kn[sb]);
     return false;
   }
   b = nb;
@@ -231,6 +240,9 @@ __device__ void decode_queue(const AttnParams& p, int u0, int u1, LDS_AS char* l
     const DecodeItem it = ldc(p.du + u);
     const ReqInfo ri = ldc(p.req + it.req);
     const int rows = ri.qo * g;
+    // Q^T fragments (inline-asm loads, covered by the first step's wait).  A
+    // column past the group's last row reads row 0's query: it computes a
+    // finite copy of that row, and its results are never stored.
     u32x4 qf[NCG][C::KS];
 #pragma unroll
     for (int j = 0; j < NCG; ++j) {
@@ -240,11 +252,7 @@ __device__ void decode_queue(const AttnParams& p, int u0, int u1, LDS_AS char* l
       const int h = it.hk * g + (ok ? row % g : 0);
       ln.lim[j] = min(it.k1, p.causal ? ri.kv - ri.qo + t + 1 : ri.kv);
       const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)(ri.qo_start + t) * p.H_q + h) * D + 8 * q;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const u32x4 v = *(const u32x4*)(qp + 32 * ks);
-        qf[j][ks] = ok ? v : u32x4{0, 0, 0, 0};
-      }
+      load_frags64<C::KS>(qp, qf[j]);
     }
     ln.mask_from = min(it.k1, p.causal ? ri.kv - ri.qo + it.c0 / g + 1 : ri.kv);
     DecodeAcc<D, NCG> a;

@@ -84,6 +84,42 @@ __device__ __forceinline__ void load_lds16_nt(const void* src, LDS_AS char* lds)
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(m0) : "memory");
 }
 
+// N 16-byte fragments 64 bytes apart (src, src + 64, ...) into registers,
+// issued from inline asm.  The loads are asynchronous and invisible to the
+// compiler: it takes the registers as written when the asm ends, so the
+// caller must wait for them itself (s_waitcnt vmcnt) and then pin them
+// (pin_regs) before any instruction reads them.  Used where the compiler's
+// own wait insertion, which cannot count the direct-to-LDS loads above,
+// would otherwise wait for loads of later steps as well.
+template <int N>
+__device__ __forceinline__ void load_frags64(const void* src, u32x4 (&f)[N]);
+template <>
+__device__ __forceinline__ void load_frags64<4>(const void* src, u32x4 (&f)[4]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %4, off\n\t"
+      "global_load_dwordx4 %1, %4, off offset:64\n\t"
+      "global_load_dwordx4 %2, %4, off offset:128\n\t"
+      "global_load_dwordx4 %3, %4, off offset:192"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+      : "v"(src));
+}
+template <>
+__device__ __forceinline__ void load_frags64<2>(const void* src, u32x4 (&f)[2]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %2, off\n\t"
+      "global_load_dwordx4 %1, %2, off offset:64"
+      : "=&v"(f[0]), "=&v"(f[1])
+      : "v"(src));
+}
+// After the s_waitcnt that covers their loads: from here on the compiler
+// sees the registers as defined by this (empty) asm, which it keeps after the
+// wait, so no read of them can move above it.
+template <int N>
+__device__ __forceinline__ void pin_regs(u32x4 (&f)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(f[i]));
+}
+
 // Reductions across lane l and lane l ^ 32 / l ^ 16 (v_permlane*_swap).
 __device__ __forceinline__ float max_x32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -1,4 +1,5 @@
-"""Static checks of the generated gfx950 code of the 32-row MLA kernel.
+"""Static checks of generated gfx950 code: the 32-row MLA kernel, and the
+attention kernel's inline-asm register loads.
 
 mla_wide.hip keeps O^T in accumulation registers that only its inline asm
 names, and places by hand the wait states that the compiler's hazard
@@ -11,6 +12,17 @@ assembly (device code only) and checks, in the kernel's code:
   2 wait states before it (an s_nop n counts n + 1, any other instruction
   1);
 * no scratch: the kernel neither spills nor uses private memory.
+
+The attention kernel's decode role loads its K and Q fragments from inline
+asm (the compiler does not see those loads, so it cannot wait for them; the
+kernel waits with explicit s_waitcnt and then pins the registers with an
+empty asm).  A copy of such a register that the compiler placed between the
+load and the wait would read data still in flight, so for the attention
+kernels this module also checks:
+
+* every instruction that reads a register written by an inline-asm
+  global_load_dwordx4, up to the next write of that register, is a matrix
+  product (the only consumer the source gives those fragments).
 
 build.py runs it after every build; tests/test_host_isa.py runs it too.
 """
@@ -93,6 +105,52 @@ def check_asm(asm: str, kernel: str = KERNEL) -> list:
     return problems
 
 
+ATTN_KERNELS = ("attn_bf16_kernelILi128", "attn_bf16_kernelILi64")
+_NO_DEST = ("global_store", "buffer_store", "flat_store", "scratch_store", "ds_write", "ds_add", "ds_store",
+            "global_atomic", "buffer_atomic", "s_", "global_load_lds", "buffer_load_lds")
+_ANY_REG = re.compile(r"\b([va])\[(\d+):(\d+)\]|\b([va])(\d+)\b")
+
+
+def _all_regs(text: str) -> set:
+    out = set()
+    for m in _ANY_REG.finditer(text):
+        if m.group(1):
+            out.update((m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1))
+        else:
+            out.add((m.group(4), int(m.group(5))))
+    return out
+
+
+def _reads_writes(text: str):
+    op = text.split()[0]
+    rest = text.split(None, 1)[1] if " " in text else ""
+    if not rest or op.startswith(_NO_DEST):
+        return _all_regs(rest), set()
+    ops = rest.split(",")
+    return _all_regs(",".join(ops[1:])), _all_regs(ops[0])
+
+
+def check_asm_loads(asm: str, kernel: str) -> list:
+    """Readers other than matrix products of registers loaded by inline asm."""
+    body = kernel_lines(asm, kernel)
+    if not body:
+        return [f"kernel {kernel} not found in the assembly"]
+    loads = [(i, _reads_writes(t)[1]) for i, (t, in_asm) in enumerate(body)
+             if in_asm and t.startswith("global_load_dwordx4")]
+    if not loads:
+        return [f"{kernel}: no inline-asm register loads found"]
+    problems = []
+    for i, dst in loads:
+        for text, _ in body[i + 1:]:
+            rd, wr = _reads_writes(text)
+            if rd & dst and not text.startswith("v_mfma"):
+                problems.append(f"{kernel}: {text!r} reads a register of {body[i][0]!r} (only matrix products may)")
+                break
+            if wr & dst:
+                break
+    return problems
+
+
 def compile_to_asm(hipcc: str, common_flags: list, src: str) -> str:
     with tempfile.TemporaryDirectory(prefix="pd_isa_") as d:
         out = os.path.join(d, "k.s")
@@ -104,8 +162,13 @@ def compile_to_asm(hipcc: str, common_flags: list, src: str) -> str:
 
 
 def run(hipcc: str, common_flags: list) -> None:
-    """Compile mla_wide.hip to assembly and raise if a check fails."""
+    """Compile mla_wide.hip and attention.hip to assembly and raise if a check
+    fails."""
     asm = compile_to_asm(hipcc, common_flags, os.path.join(HERE, "csrc", "mla_wide.hip"))
     problems = check_asm(asm)
     if problems:
         raise RuntimeError("mla_wide_kernel code check failed:\n  " + "\n  ".join(problems[:20]))
+    asm = compile_to_asm(hipcc, common_flags, os.path.join(HERE, "csrc", "attention.hip"))
+    problems = [p for k in ATTN_KERNELS for p in check_asm_loads(asm, k)]
+    if problems:
+        raise RuntimeError("attention kernel code check failed:\n  " + "\n  ".join(problems[:20]))

@@ -59,3 +59,41 @@ def test_planted_scratch_is_caught(asm_and_checker):
     asm, chk = asm_and_checker
     bad = asm.replace(".amdhsa_private_segment_fixed_size 0", ".amdhsa_private_segment_fixed_size 16")
     assert any("scratch" in p for p in chk.check_asm(bad))
+
+
+@pytest.fixture(scope="module")
+def attn_asm():
+    build = _load("_pd_build_t2", os.path.join(PKG, "build.py"))
+    try:
+        hipcc = build.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    chk = _load("_pd_isa_t2", os.path.join(PKG, "isa_check.py"))
+    return chk.compile_to_asm(hipcc, build.COMMON, os.path.join(PKG, "csrc", "attention.hip")), chk
+
+
+def test_attention_asm_loads_feed_only_matrix_products(attn_asm):
+    asm, chk = attn_asm
+    for k in chk.ATTN_KERNELS:
+        body = chk.kernel_lines(asm, k)
+        # K fragments (2 x D/32 per step) and Q fragments come from inline asm
+        assert sum(1 for t, a in body if a and t.startswith("global_load_dwordx4")) >= 8
+        assert chk.check_asm_loads(asm, k) == []
+
+
+def test_planted_copy_of_an_asm_load_is_caught(attn_asm):
+    asm, chk = attn_asm
+    lines = asm.splitlines()
+    start = next(i for i, l in enumerate(lines) if l.startswith("_Z") and chk.ATTN_KERNELS[0] in l)
+    in_asm = False
+    for i in range(start, len(lines)):
+        s = lines[i].strip()
+        in_asm = True if s.startswith(";;#ASMSTART") else False if s.startswith(";;#ASMEND") else in_asm
+        if in_asm and s.startswith("global_load_dwordx4"):
+            reg = s.split()[1].split("[")[1].split(":")[0]
+            break
+    # a copy of the loaded register placed right after the load asm
+    j = next(k for k in range(i, len(lines)) if lines[k].strip().startswith(";;#ASMEND"))
+    lines.insert(j + 1, f"\tv_mov_b32_e32 v0, v{reg}")
+    probs = chk.check_asm_loads("\n".join(lines), chk.ATTN_KERNELS[0])
+    assert probs and "reads a register" in probs[0]
