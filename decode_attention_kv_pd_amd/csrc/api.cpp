@@ -344,7 +344,8 @@ pd_status build_decode(pd_plan_s& P, const pd_plan_options* opts, int num_cus, i
     for (const QEntry& e : queues[c][q]) {
       const DecodeGroup& gr = groups[e.grp];
       const auto& pc = gr.pieces[e.piece];
-      P.du.push_back({gr.r, gr.hk, pc.first, pc.second, gr.part0 + e.piece * gr.rows + c0, c0, kClsNcg[c], 0});
+      P.du.push_back({gr.r, gr.hk, pc.first, pc.second, gr.part0 + e.piece * gr.rows + c0, c0, kClsNcg[c],
+                      c == 2 ? 1 : 0});
       block_cost[s / pdk::kWavesPerBlock] += 2.0 * (pc.second - pc.first) * D * elt;
     }
     P.dq.push_back((int32_t)P.du.size());

@@ -64,33 +64,44 @@ __device__ __forceinline__ int2 decode_pages(const AttnParams& p, const ReqInfo&
   return make_int2(ldc(pages + (min(b, kvm1) >> p.ps_shift)), ldc(pages + (min(b + 16, kvm1) >> p.ps_shift)));
 }
 
-// Loads of one 32-key step at key b: K fragments into `kf`, V rows into the
-// LDS stage, all from inline asm (2 KS + VLOADS loads, in this order), so
-// the step loop alone decides how long to wait for them.  Keys >= kv (only
-// in the request's last step) are read from row kv - 1 instead (finite data,
-// masked later), so tail slots are never read.
+// Loads of one 32-key step at key b, all from inline asm, so that the step
+// loop alone decides how long to wait for them.  Keys >= kv (only in the
+// request's last step) are read from row kv - 1 instead (finite data, masked
+// later), so tail slots are never read.
+// K fragments of the 16-key half sb into `kf` (KS loads); `page` holds key
+// b + 16 sb.
 template <int D>
-__device__ __forceinline__ void decode_issue(const AttnParams& p, const ReqInfo& ri, int hk, int b, int2 pg,
-                                             int lane, u32x4 (&kf)[2][D / 32], LDS_AS char* stage) {
+__device__ __forceinline__ void decode_issue_k(const AttnParams& p, const ReqInfo& ri, int hk, int b, int page,
+                                               int sb, int lane, u32x4 (&kf)[D / 32]) {
   using C = DecodeCfg<D>;
-  const char* pool = (const char*)p.pool;
-  const int psm = p.ps - 1;
   const int n = lane & 15, q = lane >> 4;
+  const char* kb = (const char*)p.pool + page_head_off(p, page, 0, hk);
+  const int krow = min(b + 16 * sb + n, ri.kv - 1) & (p.ps - 1);
+  load_frags64<C::KS>(kb + krow * 2 * D + 16 * q, kf);
+}
+// V rows of the 16-key half sb (keys b + 16 sb ...) into its part of the LDS
+// stage (VLOADS / 2 loads); `page` holds key b + 16 sb.
+template <int D>
+__device__ __forceinline__ void decode_issue_v(const AttnParams& p, const ReqInfo& ri, int hk, int b, int page,
+                                               int sb, int lane, LDS_AS char* stage) {
+  using C = DecodeCfg<D>;
+  const char* vb = (const char*)p.pool + page_head_off(p, page, 1, hk);
   const int kvm1 = ri.kv - 1;
   const int r = Lds<D>::dma_row(lane), c = Lds<D>::dma_chunk(lane);
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    const int j0 = b + 16 * sb;
-    const int page = sb ? pg.y : pg.x;
-    const char* kb = pool + page_head_off(p, page, 0, hk);
-    const char* vb = pool + page_head_off(p, page, 1, hk);
-    const int krow = min(j0 + n, kvm1) & psm;
-    load_frags64<C::KS>(kb + krow * 2 * D + 16 * q, kf[sb]);
+  for (int i = 0; i < C::VLOADS / 2; ++i) {
+    const int vrow = min(b + 16 * sb + i * C::RPB + r, kvm1) & (p.ps - 1);
+    load_lds16_nt(vb + vrow * 2 * D + 16 * c, stage + (sb * (C::VLOADS / 2) + i) * Lds<D>::BLOCK);
+  }
+}
+// K and V of both halves, half by half: 2 KS + VLOADS loads.
+template <int D>
+__device__ __forceinline__ void decode_issue(const AttnParams& p, const ReqInfo& ri, int hk, int b, int2 pg,
+                                             int lane, u32x4 (&kf)[2][D / 32], LDS_AS char* stage) {
 #pragma unroll
-    for (int i = 0; i < C::VLOADS / 2; ++i) {
-      const int vrow = min(j0 + i * C::RPB + r, kvm1) & psm;
-      load_lds16_nt(vb + vrow * 2 * D + 16 * c, stage + (sb * (C::VLOADS / 2) + i) * Lds<D>::BLOCK);
-    }
+  for (int sb = 0; sb < 2; ++sb) {
+    decode_issue_k<D>(p, ri, hk, b, sb ? pg.y : pg.x, sb, lane, kf[sb]);
+    decode_issue_v<D>(p, ri, hk, b, sb ? pg.y : pg.x, sb, lane, stage);
   }
 }
 
@@ -112,10 +123,11 @@ struct DecodeAcc {
 };
 
 // S, softmax and PV of the 32-key step at key b (K in kc, V in LDS stage st).
-template <int D, int NCG>
+// `before_v` runs after the softmax, before the first read of the V stage.
+template <int D, int NCG, class BeforeV>
 __device__ __forceinline__ void decode_compute(const AttnParams& p, int b, const DecodeLanes<NCG>& ln,
                                                const u32x4 (&qf)[NCG][D / 32], const u32x4 (&kc)[2][D / 32],
-                                               const LDS_AS char* st, DecodeAcc<D, NCG>& a) {
+                                               const LDS_AS char* st, DecodeAcc<D, NCG>& a, BeforeV&& before_v) {
   using C = DecodeCfg<D>;
   const float cl = p.c_log2;
   // S^T for keys b + 16 sb + 4 q + i, column lane & 15 of group j
@@ -174,6 +186,7 @@ __device__ __forceinline__ void decode_compute(const AttnParams& p, int b, const
     pb[j] = u32x4{pk[0], pk[1], pk[2], pk[3]};
     a.l[j] = mfma16(u32x4{kBf16OnesPair, kBf16OnesPair, kBf16OnesPair, kBf16OnesPair}, pb[j], a.l[j]);
   }
+  before_v();
   // V^T[d = 16 db + (lane & 15)][keys 4q + e, 16 + 4q + e]
   const LDS_AS char* vp = st + ln.v_off;
 #pragma unroll
@@ -208,7 +221,7 @@ __device__ __forceinline__ bool decode_step(const AttnParams& p, const ReqInfo& 
 #pragma unroll
   for (int j = 0; j < NCG; ++j) pin_regs(qf[j]);
   const int2 pg_after = decode_pages(p, ri, nb + 32);  // scalar loads, used next step
-  decode_compute<D, NCG>(p, b, ln, qf, kc, st, a);
+  decode_compute<D, NCG>(p, b, ln, qf, kc, st, a, [] {});
   if (!more) {
     // the repeated loads have landed; kn stays live up to here, so that the
     // compiler places nothing else in its registers while they are in flight
@@ -223,46 +236,81 @@ __device__ __forceinline__ bool decode_step(const AttnParams& p, const ReqInfo& 
   return true;
 }
 
+// Start of a unit: Q^T fragments (inline-asm loads, covered by the first
+// step's wait), the lanes' key limits, zero accumulators.  A column past the
+// group's last row reads row 0's query: it computes a finite copy of that
+// row, and its results are never stored.
+template <int D, int NCG>
+__device__ __forceinline__ void decode_unit_begin(const AttnParams& p, const DecodeItem& it, const ReqInfo& ri,
+                                                  int lane, DecodeLanes<NCG>& ln, u32x4 (&qf)[NCG][D / 32],
+                                                  DecodeAcc<D, NCG>& a) {
+  using C = DecodeCfg<D>;
+  const int n = lane & 15, q = lane >> 4;
+  const int g = p.g;
+  const int rows = ri.qo * g;
+#pragma unroll
+  for (int j = 0; j < NCG; ++j) {
+    const int row = it.c0 + 16 * j + n;
+    const bool ok = row < rows;
+    const int t = ok ? row / g : 0;
+    const int h = it.hk * g + (ok ? row % g : 0);
+    ln.lim[j] = min(it.k1, p.causal ? ri.kv - ri.qo + t + 1 : ri.kv);
+    const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)(ri.qo_start + t) * p.H_q + h) * D + 8 * q;
+    load_frags64<C::KS>(qp, qf[j]);
+  }
+  ln.mask_from = min(it.k1, p.causal ? ri.kv - ri.qo + it.c0 / g + 1 : ri.kv);
+#pragma unroll
+  for (int j = 0; j < NCG; ++j) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) a.o[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    a.l[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    a.m[j] = -INFINITY;
+  }
+}
+
+// End of a unit: row c0 + 16 j + n to partial row part + 16 j + n.
+template <int D, int NCG>
+__device__ __forceinline__ void decode_unit_store(const AttnParams& p, const DecodeItem& it, int rows, int lane,
+                                                  const DecodeAcc<D, NCG>& a) {
+  using C = DecodeCfg<D>;
+  const int n = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < NCG; ++j) {
+    if (it.c0 + 16 * j + n < rows) {
+      const float l_tot = a.l[j][0];
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const int64_t pr = (int64_t)it.part + 16 * j + n;
+      float* po = p.part_o + pr * D + 4 * q;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) *(f32x4*)(po + 16 * db) = a.o[j][db] * inv;
+      if (q == 0) p.part_lse[pr] = l_tot > 0.f ? a.m[j] * p.sm_scale + __logf(l_tot) : -INFINITY;
+    }
+  }
+}
+
+template <int NCG>
+__device__ __forceinline__ void decode_lanes_init(DecodeLanes<NCG>& ln, int lane, int v_off) {
+  ln.q = lane >> 4;
+  ln.v_off = v_off;
+}
+
 // A wavefront's queue: units [u0, u1), each written to its partial rows.
 template <int D, int NCG>
 __device__ void decode_queue(const AttnParams& p, int u0, int u1, LDS_AS char* lds) {
   using C = DecodeCfg<D>;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, q = lane >> 4;
-  const int g = p.g;
   DecodeLanes<NCG> ln;
-  ln.q = q;
-  ln.v_off = Lds<D>::off(4 * q + (n >> 2), (n & 3) >> 1) + 8 * (n & 1);
+  decode_lanes_init(ln, lane, Lds<D>::off(4 * q + (n >> 2), (n & 3) >> 1) + 8 * (n & 1));
   u32x4 kf0[2][C::KS], kf1[2][C::KS];
   LDS_AS char* st0 = lds;
   LDS_AS char* st1 = lds + C::STAGE_BYTES;
   for (int u = u0; u < u1; ++u) {
     const DecodeItem it = ldc(p.du + u);
     const ReqInfo ri = ldc(p.req + it.req);
-    const int rows = ri.qo * g;
-    // Q^T fragments (inline-asm loads, covered by the first step's wait).  A
-    // column past the group's last row reads row 0's query: it computes a
-    // finite copy of that row, and its results are never stored.
     u32x4 qf[NCG][C::KS];
-#pragma unroll
-    for (int j = 0; j < NCG; ++j) {
-      const int row = it.c0 + 16 * j + n;
-      const bool ok = row < rows;
-      const int t = ok ? row / g : 0;
-      const int h = it.hk * g + (ok ? row % g : 0);
-      ln.lim[j] = min(it.k1, p.causal ? ri.kv - ri.qo + t + 1 : ri.kv);
-      const uint16_t* qp = (const uint16_t*)p.q + ((int64_t)(ri.qo_start + t) * p.H_q + h) * D + 8 * q;
-      load_frags64<C::KS>(qp, qf[j]);
-    }
-    ln.mask_from = min(it.k1, p.causal ? ri.kv - ri.qo + it.c0 / g + 1 : ri.kv);
     DecodeAcc<D, NCG> a;
-#pragma unroll
-    for (int j = 0; j < NCG; ++j) {
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) a.o[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-      a.l[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      a.m[j] = -INFINITY;
-    }
+    decode_unit_begin<D, NCG>(p, it, ri, lane, ln, qf, a);
     int b = it.k0;
     int2 pg = decode_pages(p, ri, b);
     int2 pg_next = decode_pages(p, ri, b + 32);
@@ -271,19 +319,145 @@ __device__ void decode_queue(const AttnParams& p, int u0, int u1, LDS_AS char* l
       if (!decode_step<D, NCG>(p, ri, it.hk, it.k1, b, pg, pg_next, lane, ln, qf, kf0, kf1, st0, st1, a)) break;
       if (!decode_step<D, NCG>(p, ri, it.hk, it.k1, b, pg, pg_next, lane, ln, qf, kf1, kf0, st1, st0, a)) break;
     }
-    // partial results: row c0 + 16 j + n to partial row part + 16 j + n
+    decode_unit_store<D, NCG>(p, it, ri.qo * p.g, lane, a);
+  }
+}
+
+// ------------------------------------------------------------------------
+// Two wavefronts on one 64-row group (rows 0..31 and 32..63 of a (request,
+// KV head) with more than 32 query rows) read the same keys.  They share
+// their LDS as four V stages: each loads one 16-key half of every step's V
+// rows, three steps ahead, and reads both halves; K goes to each one's
+// registers one step ahead, as in the single-wavefront queue.  The pair runs
+// the same units in the same order, so its steps are numbered alike (T,
+// counted over the whole queue; step T uses stage T & 3).  Two counters per
+// wavefront in LDS carry the handshake:
+//   landed = T + 1 once its half of step T's V is in the stage (written
+//            after the wait that covers those loads);
+//   read   = T + 1 once its reads of stage T & 3 are issued (LDS executes a
+//            wavefront's operations in order, so a later write to the stage
+//            cannot overtake them).
+// Before reading step T's V a wavefront waits for the partner's landed >=
+// T + 1; before loading into stage (T + 3) & 3 (last read at step T - 1) it
+// waits for the partner's read >= T.  Each wait only needs an event that the
+// partner reaches without waiting for a later event of this wavefront, so
+// the pair cannot deadlock; the waits are bounded all the same.
+// ------------------------------------------------------------------------
+constexpr int kPairSpinLimit = 1 << 16;  // s_sleep 1 rounds (~64 clocks each, ~4 ms in all) before a wait gives up
+
+__device__ __forceinline__ void pair_wait(const volatile LDS_AS int32_t* f, int target) {
+  for (int i = 0; i < kPairSpinLimit; ++i) {
+    if (__builtin_amdgcn_readfirstlane(*f) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");  // nothing of the stage is read before the counter
+}
+__device__ __forceinline__ void pair_signal(volatile LDS_AS int32_t* f, int value) {
+  asm volatile("" ::: "memory");  // after the stage reads / the covering wait
+  *f = value;
+}
+
+// Page id of key b (clamped to the request's last key).
+__device__ __forceinline__ int decode_page(const AttnParams& p, const ReqInfo& ri, int b) {
+  return ldc(p.page_indices + ri.page_start + (min(b, ri.kv - 1) >> p.ps_shift));
+}
+
+struct PairState {
+  volatile LDS_AS int32_t* mine;    // [0] landed, [1] read
+  const volatile LDS_AS int32_t* theirs;
+  LDS_AS char* stages;              // four stages of STAGE_BYTES
+  int h;                            // the 16-key half this wavefront loads (= its row half)
+  int T;                            // steps of the queue so far
+};
+
+// One step T at key b of a paired unit: issue K of the next step and this
+// wavefront's V half of step T + 3 (the unit's last step again past its
+// end), wait for this step's K and V half, compute.
+template <int D>
+__device__ __forceinline__ bool decode_step_pair(const AttnParams& p, const ReqInfo& ri, int hk, int k1, int blast,
+                                                 int& b, int2& pg, int2& pg_next, int& vpg, int& vpg_next,
+                                                 int lane, const DecodeLanes<2>& ln, u32x4 (&qf)[2][D / 32],
+                                                 u32x4 (&kc)[2][D / 32], u32x4 (&kn)[2][D / 32], PairState& ps,
+                                                 DecodeAcc<D, 2>& a) {
+  using C = DecodeCfg<D>;
+  const int nb = b + 32;
+  const bool more = nb < k1;
+  const int T = ps.T;
+  {
+    const int kb = more ? nb : b;
+    const int2 kp = more ? pg_next : pg;
+    decode_issue_k<D>(p, ri, hk, kb, kp.x, 0, lane, kn[0]);
+    decode_issue_k<D>(p, ri, hk, kb, kp.y, 1, lane, kn[1]);
+  }
+  pair_wait(ps.theirs + 1, T);  // the partner has read stage (T + 3) & 3 at its step T - 1
+  decode_issue_v<D>(p, ri, hk, min(b + 96, blast), vpg, ps.h, lane, ps.stages + ((T + 3) & 3) * C::STAGE_BYTES);
+  // loads issued after this step's K: V half of T + 2, K of T + 1, V half of
+  // T + 3 (2 KS + VLOADS); this step's V half is older still
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::KS + C::VLOADS) : "memory");
 #pragma unroll
-    for (int j = 0; j < NCG; ++j) {
-      if (it.c0 + 16 * j + n < rows) {
-        const float l_tot = a.l[j][0];
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        const int64_t pr = (int64_t)it.part + 16 * j + n;
-        float* po = p.part_o + pr * D + 4 * q;
+  for (int sb = 0; sb < 2; ++sb) pin_regs(kc[sb]);
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) *(f32x4*)(po + 16 * db) = a.o[j][db] * inv;
-        if (q == 0) p.part_lse[pr] = l_tot > 0.f ? a.m[j] * p.sm_scale + __logf(l_tot) : -INFINITY;
-      }
+  for (int j = 0; j < 2; ++j) pin_regs(qf[j]);
+  pair_signal(ps.mine, T + 1);
+  const int2 pg_after = decode_pages(p, ri, nb + 32);             // K pages of the step after next
+  // V page of step T + 5 (issued two steps from now, at step T + 2)
+  const int vpg_after = decode_page(p, ri, min(b + 160, blast) + 16 * ps.h);
+  decode_compute<D, 2>(p, b, ln, qf, kc, ps.stages + (T & 3) * C::STAGE_BYTES, a,
+                       [&] { pair_wait(ps.theirs, T + 1); });
+  pair_signal(ps.mine + 1, T + 1);
+  ps.T = T + 1;
+  if (!more) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) pin_regs(kn[sb]);
+    return false;
+  }
+  b = nb;
+  pg = pg_next;
+  pg_next = pg_after;
+  vpg = vpg_next;
+  vpg_next = vpg_after;
+  return true;
+}
+
+template <int D>
+__device__ void decode_queue_pair(const AttnParams& p, int u0, int u1, PairState ps) {
+  using C = DecodeCfg<D>;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, q = lane >> 4;
+  DecodeLanes<2> ln;
+  decode_lanes_init(ln, lane, Lds<D>::off(4 * q + (n >> 2), (n & 3) >> 1) + 8 * (n & 1));
+  u32x4 kf0[2][C::KS], kf1[2][C::KS];
+  for (int u = u0; u < u1; ++u) {
+    const DecodeItem it = ldc(p.du + u);
+    const ReqInfo ri = ldc(p.req + it.req);
+    u32x4 qf[2][C::KS];
+    DecodeAcc<D, 2> a;
+    decode_unit_begin<D, 2>(p, it, ri, lane, ln, qf, a);
+    int b = it.k0;
+    const int blast = it.k0 + ((it.k1 - it.k0 - 1) & ~31);  // key of the unit's last step
+    int2 pg = decode_pages(p, ri, b);
+    decode_issue_k<D>(p, ri, it.hk, b, pg.x, 0, lane, kf0[0]);
+    decode_issue_k<D>(p, ri, it.hk, b, pg.y, 1, lane, kf0[1]);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int vb = min(b + 32 * k, blast);
+      pair_wait(ps.theirs + 1, ps.T + k - 3);
+      decode_issue_v<D>(p, ri, it.hk, vb, decode_page(p, ri, vb + 16 * ps.h), ps.h, lane,
+                        ps.stages + ((ps.T + k) & 3) * C::STAGE_BYTES);
     }
+    int2 pg_next = decode_pages(p, ri, b + 32);
+    int vpg = decode_page(p, ri, min(b + 96, blast) + 16 * ps.h);
+    int vpg_next = decode_page(p, ri, min(b + 128, blast) + 16 * ps.h);
+    for (;;) {
+      if (!decode_step_pair<D>(p, ri, it.hk, it.k1, blast, b, pg, pg_next, vpg, vpg_next, lane, ln, qf, kf0, kf1,
+                               ps, a))
+        break;
+      if (!decode_step_pair<D>(p, ri, it.hk, it.k1, blast, b, pg, pg_next, vpg, vpg_next, lane, ln, qf, kf1, kf0,
+                               ps, a))
+        break;
+    }
+    decode_unit_store<D, 2>(p, it, ri.qo * p.g, lane, a);
   }
 }
 
@@ -640,10 +814,15 @@ __device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
 
 // One launch for both roles: the block map gives each block a prefill tile
 // (v >= 0) or a decode block of eight unit queues, one per wavefront (v < 0).
+// Decode blocks keep the paired queues' counters (two per wavefront) after
+// the eight wavefronts' stages.
+template <int D>
+constexpr int decode_lds_bytes() {
+  return kAttnWaves * DecodeCfg<D>::WAVE_LDS + 2 * kAttnWaves * (int)sizeof(int32_t);
+}
 template <int D>
 constexpr int attn_lds_bytes() {
-  return PrefillCfg<D>::LDS_BYTES > kAttnWaves * DecodeCfg<D>::WAVE_LDS ? PrefillCfg<D>::LDS_BYTES
-                                                                         : kAttnWaves * DecodeCfg<D>::WAVE_LDS;
+  return PrefillCfg<D>::LDS_BYTES > decode_lds_bytes<D>() ? PrefillCfg<D>::LDS_BYTES : decode_lds_bytes<D>();
 }
 template <int D>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnParams p) {
@@ -655,14 +834,34 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnParams p
   } else {
     const int w = uniform_i(threadIdx.x >> 6);
     const int slot = (-v - 1) * kAttnWaves + w;
+    // Paired queues take the first slots of the launch, so a block holds one
+    // iff its first slot is paired.  Their counters start at zero (the
+    // barrier, taken by all eight wavefronts or none, orders this before any
+    // wavefront's first wait).
+    volatile LDS_AS int32_t* cnt = (volatile LDS_AS int32_t*)(lds + kAttnWaves * DecodeCfg<D>::WAVE_LDS);
+    {
+      const int s0 = (-v - 1) * kAttnWaves;
+      const bool paired = s0 < p.n_dq && ldc(p.dq + s0) < ldc(p.dq + s0 + 1) && ldc(p.du + ldc(p.dq + s0)).pair;
+      if (paired) {
+        if ((threadIdx.x & 63) < 2) cnt[2 * w + (threadIdx.x & 63)] = 0;
+        __syncthreads();
+      }
+    }
     if (slot < p.n_dq) {
       const int u0 = ldc(p.dq + slot), u1 = ldc(p.dq + slot + 1);
       if (u0 < u1) {
         LDS_AS char* wl = lds + w * DecodeCfg<D>::WAVE_LDS;
-        if (ldc(p.du + u0).ncg == 2)
+        const DecodeItem first = ldc(p.du + u0);
+        if (first.pair) {
+          // slots 2 i and 2 i + 1 of a block: rows 0..31 and 32..63
+          const int h = w & 1;
+          PairState ps{cnt + 2 * w, cnt + 2 * (w ^ 1), lds + (w & ~1) * DecodeCfg<D>::WAVE_LDS, h, 0};
+          decode_queue_pair<D>(p, u0, u1, ps);
+        } else if (first.ncg == 2) {
           decode_queue<D, 2>(p, u0, u1, wl);
-        else
+        } else {
           decode_queue<D, 1>(p, u0, u1, wl);
+        }
       }
     }
   }

@@ -27,9 +27,11 @@ struct PrefillItem {
 // ncg) (clipped to qo * g <= kMaxDecodeRows) of (request, KV head) over keys
 // [k0, k1); row n is token n / g, head hk * g + n % g.  Row c0 + i of the
 // unit writes its partial result (normalised o and its log-sum-exp) to
-// partial row part + i.
+// partial row part + i.  pair = 1: the unit is one half (c0 = 0 or 32) of a
+// group of more than 32 rows whose two wavefronts, adjacent slots of one
+// block running the same units, share their V stages.
 struct DecodeItem {
-  int32_t req, hk, k0, k1, part, c0, ncg, rsv;
+  int32_t req, hk, k0, k1, part, c0, ncg, pair;
 };
 
 // One (request, KV head) decode row group of rows = qo * g: key chunk i's

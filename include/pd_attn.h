@@ -199,9 +199,11 @@ pd_status pd_plan_get_stats(pd_plan_t plan, pd_plan_stats* out);
  *           {request, kv_head, first token, tokens, key end (exclusive), 0,0,0}
  *   kind 1: decode units in queue order, 8 int32 each:
  *           {request, kv_head, key begin, key end (exclusive), partial row,
- *            first row c0, 16-row column groups, 0}: rows [c0, c0 + 16 *
+ *            first row c0, 16-row column groups, paired}: rows [c0, c0 + 16 *
  *           groups) of the (request, KV head)'s qo * g rows; row c0 + i
- *           writes partial row + i
+ *           writes partial row + i; paired = 1 for groups of more than 32
+ *           rows, whose two halves run in adjacent wavefronts of one block
+ *           (the same units in the same order) and share their V stages
  *   kind 2: merge groups, 4 int32 each:
  *           {request, kv_head, first partial row, chunk count}; chunk i's
  *           result for row n is partial row first + i * qo g + n

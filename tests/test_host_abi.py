@@ -242,12 +242,22 @@ def check_cover(b, plan):
     units = {}
     used_slots = set()
     first_half = {(r, hk, k0, k1): i for i, (r, hk, k0, k1, _p, c0, _n, _z) in enumerate(du.tolist()) if c0 == 0}
-    for i, (r, hk, k0, k1, part, c0, ncg, _z) in enumerate(du.tolist()):
+    paired = [bool(dq[s] < dq[s + 1] and du[dq[s], 7] == 1) for s in range(len(dq) - 1)]
+    assert paired == sorted(paired, reverse=True), "paired queues take the first slots"
+    for s in range(len(dq) - 1):
+        q = du[dq[s]:dq[s + 1]]
+        if len(q) and q[0, 7] == 1 and q[0, 5] == 0:
+            # a paired queue: the next slot (same block) runs the same units, rows 32..63
+            q2 = du[dq[s + 1]:dq[s + 2]]
+            assert s % 2 == 0 and len(q2) == len(q)
+            assert (q2[:, :4] == q[:, :4]).all() and (q2[:, 5] == 32).all() and (q2[:, 7] == 1).all()
+    for i, (r, hk, k0, k1, part, c0, ncg, pair) in enumerate(du.tolist()):
         qo, kv = int(b.qo_lens[r]), int(b.kv_lens[r])
         rows = qo * g
         assert 1 <= rows <= MAX_DECODE_ROWS
         assert k0 % 32 == 0 and 0 <= k0 < k1 <= kv
         assert ncg == (1 if rows <= 16 else 2) and c0 % 32 == 0 and c0 < rows
+        assert pair == (1 if rows > 32 else 0)
         units.setdefault((r, hk), []).append((k0, k1, part, c0, ncg, i))
         for n in range(c0, min(rows, c0 + 16 * ncg)):
             assert part + n - c0 not in used_slots
