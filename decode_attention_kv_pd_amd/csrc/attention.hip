@@ -662,7 +662,7 @@ struct PrefillLoop {
 // VALU, and PV(t).
 template <int D, bool MASK, bool NEXT>
 __device__ __forceinline__ void prefill_iter(const AttnParams& p, const ReqInfo& ri, const PrefillItem& it,
-                                             int t, int w, int lane, bool active, int lim, PrefillLanes ln,
+                                             int t, int w, int lane, int wnt, int lim, PrefillLanes ln,
                                              const u32x4 (&qf)[D / 16], LDS_AS char* kbuf, LDS_AS char* vbuf,
                                              PrefillLoop& L, f32x16 (&s_cur)[2], f32x16 (&s_next)[2],
                                              float& m_ref, float& lsum, f32x16 (&oacc)[D / 32]) {
@@ -689,7 +689,9 @@ __device__ __forceinline__ void prefill_iter(const AttnParams& p, const ReqInfo&
 #pragma unroll
     for (int j = 0; j < 3; ++j) L.pg[j] = prefill_page<D>(p, ri, it.kv_end, (t + 3 + j) * 64, w);
   }
-  if (active) {
+  if (t < wnt) {  // the wave's rows see a key of tile t
+    // S(t + 1) even when the wave will skip tile t + 1: one straight block
+    // lets the compiler interleave these products with the softmax of tile t
     if (NEXT) prefill_scores<D>(kbuf + ((t + 1) & 3) * C::TILE_BYTES, ln, qf, s_next);  // NEXT: t + 1 < ntiles
     uint32_t pk[2][8];
     prefill_softmax<D, MASK>(p, s_cur, t * 64, lim, ln, m_ref, lsum, oacc, pk);
@@ -708,7 +710,13 @@ __device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
   const int g = p.g;
   const int rows = it.nq * g;
   const int nloc = lane & 31;
-  const int n = 32 * w + nloc;
+  // Row block of this wave.  Under a causal mask a wave skips the key tiles
+  // that lie wholly above its rows (the last ones); the two wavefronts of a
+  // SIMD (w and w + 4) take complementary row blocks (rb and 7 - rb), so the
+  // skipped work is spread evenly over the SIMDs of short prompts.
+  static_assert(kAttnWaves == 8, "row blocks are paired per SIMD for 8 wavefronts");
+  const int rb = w < 4 ? w : 11 - w;
+  const int n = 32 * rb + nloc;
   const bool row_ok = n < rows;
   const int t = row_ok ? n / g : 0;
   const int h = it.hk * g + (row_ok ? n % g : 0);
@@ -761,7 +769,14 @@ __device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
   for (int j = 0; j < 3; ++j) L.pg[j] = prefill_page<D>(p, ri, it.kv_end, (2 + j) * 64, w);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  const bool active = 32 * w < rows;  // waves whose rows are all padding skip the math
+  // key tiles this wave computes: up to the limit of its last row (none for
+  // a wave whose rows are all padding)
+  int wnt = 0;
+  if (32 * rb < rows) {
+    const int tmax = min(32 * rb + 31, rows - 1) / g;
+    wnt = (min(it.kv_end, p.causal ? qpos0 + tmax + 1 : it.kv_end) + 63) >> 6;
+  }
+  const bool active = wnt > 0;
   // Scores alternate between two register sets, sa holding S(kt) at the top
   // of each unrolled pair, so no iteration copies them.
   f32x16 sa[2], sb[2];
@@ -771,7 +786,7 @@ __device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
   const int n1 = min(nplain, last);
   int kt = 0;
 #define PD_PREFILL_ITER(MASK, NEXT, T, CUR, NXT)                                                            \
-  prefill_iter<D, MASK, NEXT>(p, ri, it, T, w, lane, active, lim, ln, qf, kbuf, vbuf, L, CUR, NXT, m_ref, lsum, \
+  prefill_iter<D, MASK, NEXT>(p, ri, it, T, w, lane, wnt, lim, ln, qf, kbuf, vbuf, L, CUR, NXT, m_ref, lsum, \
                               oacc)
   for (; kt + 1 < n1; kt += 2) {
     PD_PREFILL_ITER(false, true, kt, sa, sb);
