@@ -101,7 +101,7 @@ struct pd_plan_s {
   std::vector<int32_t> dq;          // wave slot s runs units [dq[s], dq[s + 1])
   std::vector<pdk::MergeGroup> mg;
   std::vector<int32_t> block_map;  // attention launch order
-  size_t off_qo = 0, off_req = 0, off_pages = 0, off_pf = 0, off_du = 0, off_dq = 0, off_mg = 0, off_bmap = 0;
+  size_t off_qo = 0, off_req = 0, off_pages = 0, off_launch = 0, off_du = 0, off_mg = 0;
   size_t off_rows = 0;  // (page, slot) of each new row, for the append
   size_t meta_bytes = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   int64_t prefill_flops = 0, decode_bytes = 0;
@@ -474,16 +474,12 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   off = align_up(off + sizeof(pdk::ReqInfo) * P.B);
   P.off_pages = off;
   off = align_up(off + sizeof(int32_t) * P.pages.size());
-  P.off_pf = off;
-  off = align_up(off + sizeof(pdk::PrefillItem) * P.pf.size());
+  P.off_launch = off;
+  off = align_up(off + sizeof(pdk::LaunchRec) * P.block_map.size());
   P.off_du = off;
-  off = align_up(off + sizeof(pdk::DecodeItem) * P.du.size());
-  P.off_dq = off;
-  off = align_up(off + sizeof(int32_t) * P.dq.size());
+  off = align_up(off + sizeof(pdk::DecodeUnit) * P.du.size());
   P.off_mg = off;
   off = align_up(off + sizeof(pdk::MergeGroup) * P.mg.size());
-  P.off_bmap = off;
-  off = align_up(off + sizeof(int32_t) * P.block_map.size());
   P.off_rows = off;
   off = align_up(off + sizeof(int32_t) * 2 * (size_t)P.total_rows);
   P.meta_bytes = off;
@@ -500,11 +496,27 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   put(P.off_qo, P.qo_indptr.data(), sizeof(int32_t) * P.qo_indptr.size());
   put(P.off_req, P.req.data(), sizeof(pdk::ReqInfo) * P.req.size());
   put(P.off_pages, P.pages.data(), sizeof(int32_t) * P.pages.size());
-  put(P.off_pf, P.pf.data(), sizeof(pdk::PrefillItem) * P.pf.size());
-  put(P.off_du, P.du.data(), sizeof(pdk::DecodeItem) * P.du.size());
-  put(P.off_dq, P.dq.data(), sizeof(int32_t) * P.dq.size());
+  {
+    pdk::LaunchRec* lr = (pdk::LaunchRec*)(P.blob.data() + P.off_launch);
+    const int n_slots = (int)P.dq.size() - 1;
+    for (size_t i = 0; i < P.block_map.size(); ++i) {
+      const int v = P.block_map[i];
+      pdk::LaunchRec rec{};
+      rec.v = v;
+      if (v >= 0) {
+        std::memcpy(rec.w, &P.pf[v], sizeof(pdk::PrefillItem));
+        std::memcpy(rec.w + 8, &P.req[P.pf[v].req], sizeof(pdk::ReqInfo));
+      } else {
+        const int s0 = (-v - 1) * pdk::kWavesPerBlock;
+        for (int k = 0; k <= pdk::kWavesPerBlock; ++k) rec.w[k] = P.dq[std::min(s0 + k, n_slots)];
+        rec.w[9] = (s0 < n_slots && P.dq[s0] < P.dq[s0 + 1] && P.du[P.dq[s0]].pair) ? 1 : 0;
+      }
+      lr[i] = rec;
+    }
+    pdk::DecodeUnit* du = (pdk::DecodeUnit*)(P.blob.data() + P.off_du);
+    for (size_t i = 0; i < P.du.size(); ++i) du[i] = {P.du[i], P.req[P.du[i].req]};
+  }
   put(P.off_mg, P.mg.data(), sizeof(pdk::MergeGroup) * P.mg.size());
-  put(P.off_bmap, P.block_map.data(), sizeof(int32_t) * P.block_map.size());
   {
     int32_t* rp = (int32_t*)(P.blob.data() + P.off_rows);
     for (int r = 0; r < P.B; ++r) {
@@ -569,12 +581,9 @@ pdk::AttnParams attn_params(const pd_plan_s& P, void* d_ws) {
   a.qo_indptr = (const int32_t*)(ws + P.off_qo);
   a.req = (const pdk::ReqInfo*)(ws + P.off_req);
   a.page_indices = (const int32_t*)(ws + P.off_pages);
-  a.pf = (const pdk::PrefillItem*)(ws + P.off_pf);
-  a.du = (const pdk::DecodeItem*)(ws + P.off_du);
-  a.dq = (const int32_t*)(ws + P.off_dq);
-  a.n_dq = (int32_t)P.dq.size() - 1;
+  a.launch = (const pdk::LaunchRec*)(ws + P.off_launch);
+  a.du = (const pdk::DecodeUnit*)(ws + P.off_du);
   a.mg = (const pdk::MergeGroup*)(ws + P.off_mg);
-  a.block_map = (const int32_t*)(ws + P.off_bmap);
   a.n_blocks = (int32_t)P.block_map.size();
   a.part_o = (float*)(ws + P.off_part_o);
   a.part_lse = (float*)(ws + P.off_part_lse);

@@ -306,8 +306,9 @@ __device__ void decode_queue(const AttnParams& p, int u0, int u1, LDS_AS char* l
   LDS_AS char* st0 = lds;
   LDS_AS char* st1 = lds + C::STAGE_BYTES;
   for (int u = u0; u < u1; ++u) {
-    const DecodeItem it = ldc(p.du + u);
-    const ReqInfo ri = ldc(p.req + it.req);
+    const DecodeUnit du = ldc(p.du + u);
+    const DecodeItem& it = du.it;
+    const ReqInfo& ri = du.ri;
     u32x4 qf[NCG][C::KS];
     DecodeAcc<D, NCG> a;
     decode_unit_begin<D, NCG>(p, it, ri, lane, ln, qf, a);
@@ -429,8 +430,9 @@ __device__ void decode_queue_pair(const AttnParams& p, int u0, int u1, PairState
   decode_lanes_init(ln, lane, Lds<D>::off(4 * q + (n >> 2), (n & 3) >> 1) + 8 * (n & 1));
   u32x4 kf0[2][C::KS], kf1[2][C::KS];
   for (int u = u0; u < u1; ++u) {
-    const DecodeItem it = ldc(p.du + u);
-    const ReqInfo ri = ldc(p.req + it.req);
+    const DecodeUnit du = ldc(p.du + u);
+    const DecodeItem& it = du.it;
+    const ReqInfo& ri = du.ri;
     u32x4 qf[2][C::KS];
     DecodeAcc<D, 2> a;
     decode_unit_begin<D, 2>(p, it, ri, lane, ln, qf, a);
@@ -700,13 +702,11 @@ __device__ __forceinline__ void prefill_iter(const AttnParams& p, const ReqInfo&
 }
 
 template <int D>
-__device__ void prefill_tile(const AttnParams& p, int item, LDS_AS char* lds) {
+__device__ void prefill_tile(const AttnParams& p, const PrefillItem& it, const ReqInfo& ri, LDS_AS char* lds) {
   using C = PrefillCfg<D>;
   constexpr int RPB = C::RPB;
   const int lane = threadIdx.x & 63;
   const int w = uniform_i(threadIdx.x >> 6);
-  const PrefillItem it = ldc(p.pf + item);
-  const ReqInfo ri = ldc(p.req + it.req);
   const int g = p.g;
   const int rows = it.nq * g;
   const int nloc = lane & 31;
@@ -843,40 +843,35 @@ template <int D>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char lds_raw[attn_lds_bytes<D>()];
   LDS_AS char* lds = (LDS_AS char*)lds_raw;
-  const int v = ldc(p.block_map + blockIdx.x);
+  const LaunchRec* rec = p.launch + blockIdx.x;
+  const int w = uniform_i(threadIdx.x >> 6);
+  // the record and this wavefront's queue offsets (meaningful for decode
+  // blocks only) are loaded together: none depends on another
+  const int v = ldc(&rec->v);
+  const int u0 = ldc(rec->w + w), u1 = ldc(rec->w + w + 1);
   if (v >= 0) {
-    prefill_tile<D>(p, v, lds);
+    prefill_tile<D>(p, ldc((const PrefillItem*)rec->w), ldc((const ReqInfo*)(rec->w + 8)), lds);
   } else {
-    const int w = uniform_i(threadIdx.x >> 6);
-    const int slot = (-v - 1) * kAttnWaves + w;
-    // Paired queues take the first slots of the launch, so a block holds one
-    // iff its first slot is paired.  Their counters start at zero (the
-    // barrier, taken by all eight wavefronts or none, orders this before any
-    // wavefront's first wait).
+    // Paired queues take the first slots of the launch; a block that holds
+    // some zeroes their counters, and the barrier (taken by all eight
+    // wavefronts or none) orders this before any wavefront's first wait.
     volatile LDS_AS int32_t* cnt = (volatile LDS_AS int32_t*)(lds + kAttnWaves * DecodeCfg<D>::WAVE_LDS);
-    {
-      const int s0 = (-v - 1) * kAttnWaves;
-      const bool paired = s0 < p.n_dq && ldc(p.dq + s0) < ldc(p.dq + s0 + 1) && ldc(p.du + ldc(p.dq + s0)).pair;
-      if (paired) {
-        if ((threadIdx.x & 63) < 2) cnt[2 * w + (threadIdx.x & 63)] = 0;
-        __syncthreads();
-      }
+    if (ldc(rec->w + 9)) {
+      if ((threadIdx.x & 63) < 2) cnt[2 * w + (threadIdx.x & 63)] = 0;
+      __syncthreads();
     }
-    if (slot < p.n_dq) {
-      const int u0 = ldc(p.dq + slot), u1 = ldc(p.dq + slot + 1);
-      if (u0 < u1) {
-        LDS_AS char* wl = lds + w * DecodeCfg<D>::WAVE_LDS;
-        const DecodeItem first = ldc(p.du + u0);
-        if (first.pair) {
-          // slots 2 i and 2 i + 1 of a block: rows 0..31 and 32..63
-          const int h = w & 1;
-          PairState ps{cnt + 2 * w, cnt + 2 * (w ^ 1), lds + (w & ~1) * DecodeCfg<D>::WAVE_LDS, h, 0};
-          decode_queue_pair<D>(p, u0, u1, ps);
-        } else if (first.ncg == 2) {
-          decode_queue<D, 2>(p, u0, u1, wl);
-        } else {
-          decode_queue<D, 1>(p, u0, u1, wl);
-        }
+    if (u0 < u1) {
+      LDS_AS char* wl = lds + w * DecodeCfg<D>::WAVE_LDS;
+      const DecodeItem first = ldc(&p.du[u0].it);
+      if (first.pair) {
+        // slots 2 i and 2 i + 1 of a block: rows 0..31 and 32..63
+        const int h = w & 1;
+        PairState ps{cnt + 2 * w, cnt + 2 * (w ^ 1), lds + (w & ~1) * DecodeCfg<D>::WAVE_LDS, h, 0};
+        decode_queue_pair<D>(p, u0, u1, ps);
+      } else if (first.ncg == 2) {
+        decode_queue<D, 2>(p, u0, u1, wl);
+      } else {
+        decode_queue<D, 1>(p, u0, u1, wl);
       }
     }
   }
@@ -949,11 +944,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(AttnParams p) {
   constexpr int NO = D / 64;
   const int lane = threadIdx.x & 63;
   const int w = uniform_i(threadIdx.x >> 6);
-  const int v = ldc(p.block_map + blockIdx.x);
+  const LaunchRec* rec = p.launch + blockIdx.x;
+  const int v = ldc(&rec->v);
   const float* qbase = (const float*)p.q;
   if (v >= 0) {
-    const PrefillItem it = ldc(p.pf + v);
-    const ReqInfo ri = ldc(p.req + it.req);
+    const PrefillItem it = ldc((const PrefillItem*)rec->w);
+    const ReqInfo ri = ldc((const ReqInfo*)(rec->w + 8));
     const int rows = it.nq * p.g;
     for (int n = w; n < rows; n += kWavesPerBlock) {
       const int t = n / p.g, h = it.hk * p.g + n % p.g;
@@ -966,12 +962,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(AttnParams p) {
       if (lane == 0 && p.lse) p.lse[row] = lse;
     }
   } else {
-    const int slot = (-v - 1) * kWavesPerBlock + w;
-    if (slot >= p.n_dq) return;
-    const int u1 = ldc(p.dq + slot + 1);
-    for (int u = ldc(p.dq + slot); u < u1; ++u) {
-      const DecodeItem it = ldc(p.du + u);
-      const ReqInfo ri = ldc(p.req + it.req);
+    const int u1 = ldc(rec->w + w + 1);
+    for (int u = ldc(rec->w + w); u < u1; ++u) {
+      const DecodeUnit du = ldc(p.du + u);
+      const DecodeItem& it = du.it;
+      const ReqInfo& ri = du.ri;
       const int nrows = min(ri.qo * p.g, it.c0 + kDecodeCols * it.ncg);
       for (int n = it.c0; n < nrows; ++n) {
         const int t = n / p.g, h = it.hk * p.g + n % p.g;

@@ -34,6 +34,25 @@ struct DecodeItem {
   int32_t req, hk, k0, k1, part, c0, ncg, pair;
 };
 
+// What the attention kernel reads for one decode unit: the unit and its
+// request's row, in one 48-byte record (one dependent load fewer).
+struct DecodeUnit {
+  DecodeItem it;
+  ReqInfo ri;
+};
+
+// One block of the attention launch, 64 bytes, indexed by the block id (so
+// that a block's first load depends on nothing else).
+//   v >= 0: prefill tile v; w[0..7] = the tile, w[8..11] = its request's row.
+//   v < 0:  decode block -v - 1; w[0..8] = the queue offsets of its eight
+//           wavefront slots (slot k runs units [w[k], w[k + 1])), w[9] = 1
+//           when its first slots hold paired queues.
+struct LaunchRec {
+  int32_t v;
+  int32_t w[15];
+};
+static_assert(sizeof(PrefillItem) == 32 && sizeof(ReqInfo) == 16, "launch record layout");
+
 // One (request, KV head) decode row group of rows = qo * g: key chunk i's
 // partial result for row n sits in partial row part0 + i * rows + n; nparts
 // is the number of chunks.  The merge kernel combines the chunks into
@@ -58,15 +77,12 @@ struct AttnParams {
   const int32_t* qo_indptr;
   const ReqInfo* req;
   const int32_t* page_indices;
-  const PrefillItem* pf;
-  const DecodeItem* du;   // in queue order
-  const int32_t* dq;      // wavefront slot s of the decode blocks runs units [dq[s], dq[s + 1])
+  const LaunchRec* launch;  // one record per block of the attention launch
+  const DecodeUnit* du;     // decode units in queue order
   const MergeGroup* mg;
-  const int32_t* block_map;  // launch block -> prefill tile (>= 0) or decode block (-b - 1)
   float* part_o;    // [partial rows][D]
   float* part_lse;  // [partial rows]
   int32_t n_pf, n_du, n_mg, B;
-  int32_t n_dq;      // decode wavefront slots
   int32_t n_blocks;  // blocks of the attention launch
   int32_t H_q, H_kv, g, ps;
   int32_t ps_shift;  // log2(ps)
