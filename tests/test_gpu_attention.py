@@ -78,6 +78,10 @@ RAGGED = [
     ("mixed", ((1, 1, 2), (3000, 70, 1500)), dict(heads=(33, 1))),         # 33 / 33 / 66 rows
     ("mixed", ((1, 3, 2), (1800, 2000, 45)), dict(heads=(48, 3))),         # 16 / 48 / 32 rows
     ("tiny", ((5, 9, 2), (40, 300, 17)), dict(heads=(28, 4))),             # fp32: 35 / 63 / 14 rows
+    # paired 64-row groups at head_dim 64 and page 16 (their four shared V
+    # stages are 4 KiB each), with a 33-row group beside them
+    ("mixed", ((1, 1, 1), (5000, 37, 1200)), dict(heads=(64, 1), head_dim=64, page_size=16)),
+    ("mixed", ((1, 3), (2100, 900)), dict(heads=(33, 3), head_dim=64)),   # 11 / 33 rows
 ]
 
 
@@ -148,7 +152,9 @@ def test_sharpened_softmax():
 
 @pytest.mark.parametrize("chunk", [32, 96, 512])
 def test_split_count_invariance(chunk):
-    for heads in ((32, 8), (64, 2)):   # 16-row and 32/64-row decode units
+    # 16-row, 32-row and paired 64-row decode units (a forced chunk gives one
+    # unit per queue: the paired queues then hold a single unit each)
+    for heads in ((32, 8), (64, 2), (128, 2)):
         b = batch("mixed", ((1, 2, 1, 3), (4000, 3000, 2048, 700)), heads=heads)
         out0, _ = DeviceRun(b).step()
         out1, _ = check(b, f"split{chunk}_{heads}", chunk=chunk)
