@@ -5,7 +5,8 @@ library's HIP kernels; torch supplies device memory and the current stream.
 The names mirror the C entry points of include/pd_attn.h:
 
   pd_plan(desc, qo_lens, kv_lens, page_indptr, page_indices, num_pool_pages,
-          decode_chunk_keys=0, num_cus=0, block_order=0)  -> Plan  (host only)
+          decode_chunk_keys=0, num_cus=0, block_order=0,
+          prefill_block_waves=0)                   -> Plan  (host only)
   pd_plan_upload(plan, ws, stream=None)
   pd_kv_append(plan, ws, kv_pool, k_new, v_new, stream=None)
   pd_attention_run(plan, ws, q, kv_pool, out, lse=None, stream=None)
@@ -76,7 +77,8 @@ class pd_mla_desc(ctypes.Structure):
 
 class pd_plan_options(ctypes.Structure):
     _fields_ = [("decode_chunk_keys", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-                ("block_order", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
+                ("block_order", ctypes.c_int32), ("prefill_block_waves", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 4)]
 
 
 class pd_plan_stats(ctypes.Structure):
@@ -268,14 +270,15 @@ class Plan:
 
 
 def pd_plan(desc, qo_lens, kv_lens, page_indptr, page_indices, num_pool_pages,
-            decode_chunk_keys: int = 0, num_cus: int = 0, block_order: int = 0) -> Plan:
+            decode_chunk_keys: int = 0, num_cus: int = 0, block_order: int = 0,
+            prefill_block_waves: int = 0) -> Plan:
     qo, pqo = _i32(qo_lens)
     kv, pkv = _i32(kv_lens)
     ip, pip = _i32(page_indptr)
     pi, ppi = _i32(page_indices)
     if len(qo) != len(kv) or len(ip) != len(qo) + 1:
         raise ValueError("qo_lens / kv_lens / page_indptr lengths disagree")
-    opts = pd_plan_options(int(decode_chunk_keys), int(num_cus), int(block_order))
+    opts = pd_plan_options(int(decode_chunk_keys), int(num_cus), int(block_order), int(prefill_block_waves))
     h = ctypes.c_void_p()
     _check(_lib.pd_plan(ctypes.byref(desc), len(qo), pqo, pkv, pip, ppi if len(pi) else None,
                         int(num_pool_pages), ctypes.byref(opts), ctypes.byref(h)))

@@ -101,6 +101,7 @@ struct pd_plan_s {
   std::vector<int32_t> dq;          // wave slot s runs units [dq[s], dq[s + 1])
   std::vector<pdk::MergeGroup> mg;
   std::vector<int32_t> block_map;  // attention launch order
+  bool prefill4 = false;           // 128-row tiles in 4-wavefront blocks (prefill-only launches)
   size_t off_qo = 0, off_req = 0, off_pages = 0, off_launch = 0, off_du = 0, off_mg = 0;
   size_t off_rows = 0;  // (page, slot) of each new row, for the append
   size_t meta_bytes = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
@@ -360,8 +361,28 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   const int64_t elt = elt_bytes(&d);
   int num_cus = (opts && opts->num_cus > 0) ? opts->num_cus : 256;
 
-  // ---- prefill tiles: requests whose qo * g rows exceed the decode role's
-  const int T = std::max(1, pdk::kPrefillRows / g);  // tokens per tile
+  // ---- prefill tiles: requests whose qo * g rows exceed the decode role's.
+  // A launch with no decode rows whose prefill requests all have short caches
+  // (at most 64 key tiles) runs 128-row tiles in 4-wavefront blocks, two per
+  // CU; otherwise 256-row tiles in 8-wavefront blocks.
+  {
+    bool any_decode = false, any_prefill = false;
+    int max_kv = 0;
+    for (int r = 0; r < P.B; ++r) {
+      const pdk::ReqInfo& ri = P.req[r];
+      if (ri.qo == 0) continue;
+      if ((int64_t)ri.qo * g <= pdk::kMaxDecodeRows) {
+        any_decode = true;
+      } else {
+        any_prefill = true;
+        max_kv = std::max(max_kv, ri.kv);
+      }
+    }
+    const int pw = opts ? opts->prefill_block_waves : 0;
+    P.prefill4 = any_prefill && !any_decode && g <= pdk::kPrefillRows / 2 &&
+                 (pw == 4 || (pw == 0 && max_kv <= 64 * 64));
+  }
+  const int T = std::max(1, (P.prefill4 ? pdk::kPrefillRows / 2 : pdk::kPrefillRows) / g);  // tokens per tile
   std::vector<double> pf_cost;                        // flops of each tile, launch order
   struct Tile {
     pdk::PrefillItem it;
@@ -585,6 +606,7 @@ pdk::AttnParams attn_params(const pd_plan_s& P, void* d_ws) {
   a.du = (const pdk::DecodeUnit*)(ws + P.off_du);
   a.mg = (const pdk::MergeGroup*)(ws + P.off_mg);
   a.n_blocks = (int32_t)P.block_map.size();
+  a.prefill4 = P.prefill4 ? 1 : 0;
   a.part_o = (float*)(ws + P.off_part_o);
   a.part_lse = (float*)(ws + P.off_part_lse);
   a.n_pf = (int32_t)P.pf.size();
@@ -979,6 +1001,8 @@ pd_status pd_plan(const pd_attn_desc* desc, int32_t batch, const int32_t* qo_len
       return fail(PD_ERR_INVALID_ARG, "negative planner option");
     if (opts && opts->block_order != 0 && opts->block_order != 1)
       return fail(PD_ERR_INVALID_ARG, "block_order must be 0 or 1");
+    if (opts && opts->prefill_block_waves != 0 && opts->prefill_block_waves != 4 && opts->prefill_block_waves != 8)
+      return fail(PD_ERR_INVALID_ARG, "prefill_block_waves must be 0, 4 or 8");
     pd_plan_s* P = new pd_plan_s();
     s = fill_requests(*P, desc->page_size, batch, qo_lens, kv_lens, page_indptr, page_indices, num_pool_pages);
     if (s != PD_OK) {

@@ -479,24 +479,28 @@ __device__ void decode_queue_pair(const AttnParams& p, int u0, int u1, PairState
 //   same phase at the same time.  Tiles that cross the causal diagonal (or
 //   the end of the cache) run a masked copy.
 // ------------------------------------------------------------------------
-template <int D>
+// W wavefronts per block: 8 (256-row tiles, four K and V buffers, one block
+// per CU) or 4 (128-row tiles, two buffers, two blocks per CU; see
+// prefill_tile4).
+template <int D, int W = kAttnWaves>
 struct PrefillCfg {
   static constexpr int KS = D / 16;     // 16-wide k-steps of S
   static constexpr int DB = D / 32;     // 32-row d-blocks of O^T
   static constexpr int RPB = Lds<D>::RPB;
-  static constexpr int ROWS_PER_WAVE = 64 / kAttnWaves;  // K/V rows each wave loads per tile
-  static constexpr int LOADS = ROWS_PER_WAVE / RPB;      // 1 KiB loads per wave per matrix per tile
-  static constexpr int NBUF = 4;                         // K and V tile buffers (tile t in buffer t % 4)
+  static constexpr int ROWS_PER_WAVE = 64 / W;        // K/V rows each wave loads per tile
+  static constexpr int LOADS = ROWS_PER_WAVE / RPB;   // 1 KiB loads per wave per matrix per tile
+  static constexpr int NBUF = W == 8 ? 4 : 2;         // K and V tile buffers
   static constexpr int TILE_BYTES = Lds<D>::bytes(64);
   static constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
+  static_assert(LOADS >= 1 && (W == 8 || W == 4), "prefill block shape");
 };
 
 // Page id of wave w's row group of the tile at kbase (clamped to the tile's
 // last key).
-template <int D>
+template <int D, int W = kAttnWaves>
 __device__ __forceinline__ int prefill_page(const AttnParams& p, const ReqInfo& ri, int kv_end, int kbase,
                                             int w) {
-  constexpr int RW = PrefillCfg<D>::ROWS_PER_WAVE;
+  constexpr int RW = PrefillCfg<D, W>::ROWS_PER_WAVE;
   return ldc(p.page_indices + ri.page_start + (min(kbase + RW * w, kv_end - 1) >> p.ps_shift));
 }
 
@@ -504,10 +508,10 @@ __device__ __forceinline__ int prefill_page(const AttnParams& p, const ReqInfo& 
 // its 8-row group, inside one page since pages hold >= 16 aligned rows).
 // `full`: every row < kv_end; otherwise rows past kv_end - 1 are read from
 // row kv_end - 1 (finite, masked later).
-template <int D>
+template <int D, int W = kAttnWaves>
 __device__ __forceinline__ void prefill_issue(const AttnParams& p, int hk, int half, int kv_end, int kbase,
                                               int w, int page, int lane, bool full, LDS_AS char* dst) {
-  using C = PrefillCfg<D>;
+  using C = PrefillCfg<D, W>;
   const char* pool = (const char*)p.pool;
   const int psm = p.ps - 1;
   const int r = Lds<D>::dma_row(lane), c = Lds<D>::dma_chunk(lane);
@@ -827,6 +831,177 @@ __device__ void prefill_tile(const AttnParams& p, const PrefillItem& it, const R
   }
 }
 
+// ------------------------------------------------------------------------
+// Short prompts: 4-wavefront blocks of 128 query rows with two K and two V
+// tile buffers (67.6 KB of LDS at head_dim 128), so that two blocks share a
+// CU and one block's prologue (its cold Q and first K/V loads) overlaps the
+// other's tiles.  One barrier per key tile: at the start of iteration t
+// every wave waits for its loads of K(t+1) and V(t) (issued one iteration
+// earlier), the barrier publishes them, and the wave issues K(t+2) into the
+// buffer of K(t) (read by S(t) in iteration t - 1) and V(t+1) into the
+// buffer of V(t - 1) (read by PV(t - 1)).  Then S(t+1), the softmax of t and
+// PV(t), as in prefill_iter.  Each SIMD holds one wavefront of each of the
+// two blocks, so no row-block pairing is needed; a wavefront still skips
+// the key tiles wholly above its rows.
+// ------------------------------------------------------------------------
+constexpr int kPrefill4Waves = 4;
+constexpr int kPrefill4Threads = 64 * kPrefill4Waves;
+constexpr int kPrefill4Rows = 32 * kPrefill4Waves;
+
+struct Prefill4Loop {
+  int ntiles, nfull;
+  int pk, pv;  // page ids of K(t + 2) and V(t + 1) for the loads of iteration t
+};
+
+template <int D, bool MASK, bool NEXT>
+__device__ __forceinline__ void prefill_iter4(const AttnParams& p, const ReqInfo& ri, const PrefillItem& it,
+                                              int t, int w, int lane, int wnt, int lim, PrefillLanes ln,
+                                              const u32x4 (&qf)[D / 16], LDS_AS char* kbuf, LDS_AS char* vbuf,
+                                              Prefill4Loop& L, f32x16 (&s_cur)[2], f32x16 (&s_next)[2],
+                                              float& m_ref, float& lsum, f32x16 (&oacc)[D / 32]) {
+  constexpr int W = kPrefill4Waves;
+  using C = PrefillCfg<D, W>;
+  const int nt = L.ntiles;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (t + 2 < nt)
+    prefill_issue<D, W>(p, it.hk, 0, it.kv_end, (t + 2) * 64, w, L.pk, lane, t + 2 < L.nfull,
+                        kbuf + (t & 1) * C::TILE_BYTES);
+  if (t + 1 < nt)
+    prefill_issue<D, W>(p, it.hk, 1, it.kv_end, (t + 1) * 64, w, L.pv, lane, t + 1 < L.nfull,
+                        vbuf + ((t + 1) & 1) * C::TILE_BYTES);
+  // pages of the next iteration's loads: V(t + 2) lies in the tile of K(t + 2)
+  L.pv = L.pk;
+  L.pk = prefill_page<D, W>(p, ri, it.kv_end, (t + 3) * 64, w);
+  if (t < wnt) {
+    if (NEXT) prefill_scores<D>(kbuf + ((t + 1) & 1) * C::TILE_BYTES, ln, qf, s_next);
+    uint32_t pk[2][8];
+    prefill_softmax<D, MASK>(p, s_cur, t * 64, lim, ln, m_ref, lsum, oacc, pk);
+    prefill_pv<D>(vbuf + (t & 1) * C::TILE_BYTES, ln, pk, oacc);
+  }
+}
+
+template <int D>
+__device__ void prefill_tile4(const AttnParams& p, const PrefillItem& it, const ReqInfo& ri, LDS_AS char* lds) {
+  constexpr int W = kPrefill4Waves;
+  using C = PrefillCfg<D, W>;
+  const int lane = threadIdx.x & 63;
+  const int w = uniform_i(threadIdx.x >> 6);
+  const int g = p.g;
+  const int rows = it.nq * g;
+  const int nloc = lane & 31;
+  const int n = 32 * w + nloc;
+  const bool row_ok = n < rows;
+  const int t = row_ok ? n / g : 0;
+  const int h = it.hk * g + (row_ok ? n % g : 0);
+  const int qpos0 = ri.kv - ri.qo + it.q0;
+  const int lim = p.causal ? qpos0 + t + 1 : ri.kv;
+  const int mask_from = p.causal ? qpos0 + 1 : it.kv_end;
+  const int64_t qrow = (int64_t)(ri.qo_start + it.q0 + t) * p.H_q + h;
+
+  PrefillLanes ln;
+  ln.h2 = lane >> 5;
+  ln.k_off = Lds<D>::off(nloc, ln.h2);
+  {
+    const int j = lane & 15, dhalf = (lane >> 4) & 1;
+    ln.v_off = Lds<D>::off(4 * ln.h2 + (j >> 2), 2 * dhalf + ((j & 3) >> 1)) + 8 * (j & 1);
+  }
+  u32x4 qf[C::KS];
+  {
+    const uint16_t* qp = (const uint16_t*)p.q + qrow * D + 8 * ln.h2;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const u32x4 v = *(const u32x4*)(qp + 16 * ks);
+      qf[ks] = row_ok ? v : u32x4{0, 0, 0, 0};
+    }
+  }
+  f32x16 oacc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
+  float m_ref = -INFINITY;
+  float lsum = 0.f;
+
+  LDS_AS char* kbuf = lds;
+  LDS_AS char* vbuf = lds + C::NBUF * C::TILE_BYTES;
+  const int ntiles = (it.kv_end + 63) >> 6;
+  const int nfull = it.kv_end >> 6;
+  const int nplain = min(ntiles, mask_from / 64);
+  // prologue: K(0) V(0) K(1), and the pages of iteration 0's loads
+  Prefill4Loop L;
+  L.ntiles = ntiles;
+  L.nfull = nfull;
+  {
+    const int pg0 = prefill_page<D, W>(p, ri, it.kv_end, 0, w);
+    prefill_issue<D, W>(p, it.hk, 0, it.kv_end, 0, w, pg0, lane, 0 < nfull, kbuf);
+    prefill_issue<D, W>(p, it.hk, 1, it.kv_end, 0, w, pg0, lane, 0 < nfull, vbuf);
+    const int pg1 = prefill_page<D, W>(p, ri, it.kv_end, 64, w);
+    if (ntiles > 1) prefill_issue<D, W>(p, it.hk, 0, it.kv_end, 64, w, pg1, lane, 1 < nfull, kbuf + C::TILE_BYTES);
+    L.pv = pg1;
+    L.pk = prefill_page<D, W>(p, ri, it.kv_end, 128, w);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int wnt = 0;
+  if (32 * w < rows) {
+    const int tmax = min(32 * w + 31, rows - 1) / g;
+    wnt = (min(it.kv_end, p.causal ? qpos0 + tmax + 1 : it.kv_end) + 63) >> 6;
+  }
+  f32x16 sa[2], sb[2];
+  if (wnt > 0) prefill_scores<D>(kbuf, ln, qf, sa);
+  const int last = ntiles - 1;
+  const int n1 = min(nplain, last);
+  int kt = 0;
+#define PD_PREFILL4_ITER(MASK, NEXT, T, CUR, NXT)                                                            \
+  prefill_iter4<D, MASK, NEXT>(p, ri, it, T, w, lane, wnt, lim, ln, qf, kbuf, vbuf, L, CUR, NXT, m_ref, lsum, \
+                               oacc)
+  for (; kt + 1 < n1; kt += 2) {
+    PD_PREFILL4_ITER(false, true, kt, sa, sb);
+    PD_PREFILL4_ITER(false, true, kt + 1, sb, sa);
+  }
+  if (kt < n1) {
+    PD_PREFILL4_ITER(false, true, kt, sa, sb);
+    ++kt;
+    sa[0] = sb[0];
+    sa[1] = sb[1];
+  }
+  for (; kt + 1 < last; kt += 2) {
+    PD_PREFILL4_ITER(true, true, kt, sa, sb);
+    PD_PREFILL4_ITER(true, true, kt + 1, sb, sa);
+  }
+  if (kt < last) {
+    PD_PREFILL4_ITER(true, true, kt, sa, sb);
+    sa[0] = sb[0];
+    sa[1] = sb[1];
+  }
+  if (last < nplain)
+    PD_PREFILL4_ITER(false, false, last, sa, sb);
+  else
+    PD_PREFILL4_ITER(true, false, last, sa, sb);
+#undef PD_PREFILL4_ITER
+  const float l_tot = sum_x32(lsum);
+  if (row_ok) {
+    const float inv = 1.f / l_tot;
+    float* op = p.out + qrow * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 v = {oacc[db][4 * jj + 0], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
+        *(f32x4*)(op + 32 * db + 8 * jj + 4 * ln.h2) = v * inv;
+      }
+    if (ln.h2 == 0 && p.lse) p.lse[qrow] = m_ref * p.sm_scale + __logf(l_tot);
+  }
+}
+
+// Prefill-only launches of 128-row tiles (the plan's launch records all hold
+// one tile): two blocks per CU.
+template <int D>
+__global__ __launch_bounds__(kPrefill4Threads, 2) void attn_prefill4_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) char lds_raw[PrefillCfg<D, kPrefill4Waves>::LDS_BYTES];
+  const LaunchRec* rec = p.launch + blockIdx.x;
+  prefill_tile4<D>(p, ldc((const PrefillItem*)rec->w), ldc((const ReqInfo*)(rec->w + 8)), (LDS_AS char*)lds_raw);
+}
+
 // One launch for both roles: the block map gives each block a prefill tile
 // (v >= 0) or a decode block of eight unit queues, one per wavefront (v < 0).
 // Decode blocks keep the paired queues' counters (two per wavefront) after
@@ -1023,7 +1198,12 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(AttnParams p) {
 hipError_t launch_attention(const AttnParams& p, int dtype, hipStream_t s) {
   const int blocks = p.n_blocks;
   if (blocks == 0) return hipSuccess;
-  if (dtype == 1) {
+  if (dtype == 1 && p.prefill4) {
+    if (p.D == 128)
+      hipLaunchKernelGGL(attn_prefill4_kernel<128>, dim3(blocks), dim3(kPrefill4Threads), 0, s, p);
+    else
+      hipLaunchKernelGGL(attn_prefill4_kernel<64>, dim3(blocks), dim3(kPrefill4Threads), 0, s, p);
+  } else if (dtype == 1) {
     if (p.D == 128)
       hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(blocks), dim3(kAttnThreads), 0, s, p);
     else

@@ -84,6 +84,7 @@ struct AttnParams {
   float* part_lse;  // [partial rows]
   int32_t n_pf, n_du, n_mg, B;
   int32_t n_blocks;  // blocks of the attention launch
+  int32_t prefill4;  // prefill-only launch of 128-row tiles in 4-wavefront blocks
   int32_t H_q, H_kv, g, ps;
   int32_t ps_shift;  // log2(ps)
   int32_t D, causal;

@@ -119,12 +119,21 @@ typedef struct pd_attn_desc {
  *                          cost at peak rates (default: CUs running decode
  *                          blocks stream the cache while the others run
  *                          prefill tiles); 1 = all prefill tiles, then all
- *                          decode blocks                                   */
+ *                          decode blocks
+ *   prefill_block_waves 0 (default): a launch with no decode rows whose
+ *                      prefill requests all have at most 4096 cached keys
+ *                      (short prompts) runs 128-row query tiles in blocks of
+ *                      4 wavefronts, two blocks per compute unit, so that
+ *                      one block's first loads overlap the other's work;
+ *                      any other launch runs 256-row tiles in blocks of 8.
+ *                      4: the 4-wavefront form whenever the launch has no
+ *                      decode rows (and g <= 128); 8: always 256-row tiles */
 typedef struct pd_plan_options {
   int32_t decode_chunk_keys;
   int32_t num_cus;
   int32_t block_order;
-  int32_t reserved[5];
+  int32_t prefill_block_waves;
+  int32_t reserved[4];
 } pd_plan_options;
 
 /* Plan statistics (pd_plan_get_stats). */

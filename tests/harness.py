@@ -55,12 +55,13 @@ class DeviceRun:
     """One step of the path on the GPU for a materialised batch."""
 
     def __init__(self, b: Batch, decode_chunk_keys: int = 0, pool: np.ndarray = None,
-                 device="cuda", num_cus: int = 0):
+                 device="cuda", num_cus: int = 0, prefill_block_waves: int = 0):
         m = pd()
         self.b = b
         self.desc = desc_of(b)
         self.plan = m.pd_plan(self.desc, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices,
-                              b.num_pool_pages, decode_chunk_keys=decode_chunk_keys, num_cus=num_cus)
+                              b.num_pool_pages, decode_chunk_keys=decode_chunk_keys, num_cus=num_cus,
+                              prefill_block_waves=prefill_block_waves)
         self.ws = torch.empty(max(self.plan.workspace_bytes, 1), dtype=torch.uint8, device=device)
         m.pd_plan_upload(self.plan, self.ws)
         self.pool_host = prefix_pool(b) if pool is None else pool

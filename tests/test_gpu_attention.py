@@ -188,6 +188,38 @@ def test_decode_queues_of_many_units(idx):
     assert np.abs(lse - L).max() <= lse_tol(b) + 2.0 ** -20 * np.abs(L).max()
 
 
+PREFILL4_CASES = [
+    # prefill-only batches in 128-row tiles of 4-wavefront blocks (two blocks
+    # per CU): g = 1 / 4 / 32 (32 / 4 tokens per tile), head_dim 64,
+    # non-causal, chunks over cached keys, caches past the automatic limit
+    ("prefill", None, {}),                                                  # the 8 x 512 workload (default plan)
+    ("prefill", ((300, 513, 129, 700), (300, 513, 129, 700)), dict(heads=(8, 8))),
+    ("prefill", ((257, 90), (1000, 800)), dict(heads=(16, 4))),             # chunked prefill over cached keys
+    ("prefill", ((400, 70), (400, 900)), dict(heads=(8, 2), causal=False)),
+    ("prefill", ((320, 513), (320, 513)), dict(heads=(8, 8), head_dim=64, page_size=64)),
+    ("prefill", ((37, 300), (900, 5000)), dict(heads=(32, 1), page_size=64)),  # g = 32: 4-token tiles
+    ("prefill", ((3000, 65), (9000, 100)), dict(heads=(8, 8))),             # long caches, a 65-row tail tile
+]
+
+
+@pytest.mark.parametrize("idx", range(len(PREFILL4_CASES)))
+def test_prefill_four_wave_blocks(idx):
+    wid, lengths, kw = PREFILL4_CASES[idx]
+    b = batch(wid, lengths, **kw)
+    run = DeviceRun(b, prefill_block_waves=4)
+    pf = run.plan.work_items(0)
+    assert len(pf) and (pf[:, 3] * (b.H_q // b.H_kv) <= 128).all()
+    print(f"case pf4_{idx}: {len(pf)} tiles of <= 128 rows", flush=True)
+    out, lse = run.step()
+    O, L = oracle_outputs(b)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    assert report(f"pf4_{idx}", out, O) <= tolerance(b)
+    assert np.abs(lse - L).max() <= lse_tol(b) + 2.0 ** -20 * np.abs(L).max()
+    # 256-row tiles of 8-wavefront blocks give the same rows to rounding
+    out8, _ = DeviceRun(b, prefill_block_waves=8).step()
+    assert np.abs(out8 - out).max() <= tolerance(b)
+
+
 def test_bitwise_deterministic_for_a_fixed_plan():
     b = batch("mixed", ((300, 1, 1, 2), (300, 4000, 1500, 700)))
     run = DeviceRun(b)

@@ -372,6 +372,34 @@ def test_block_map_covers_work_and_keeps_xcd_affinity(order):
         assert (bmap[:len(pf)] >= 0).all()
 
 
+def test_prefill_block_shape_for_short_prompts():
+    """Prefill-only launches of short caches run 128-row tiles (4-wavefront
+    blocks, two per CU); 8 keeps 256-row tiles; a launch with decode rows,
+    or a cache past 4096 keys without the option, keeps 256-row tiles."""
+    def plan_of(wid, **kw):
+        lengths = kw.pop("lengths", None)
+        b = make_batch(wid, materialize=False, lengths=lengths)
+        d = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype, b.causal)
+        return b, pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages, **kw)
+    b, p = plan_of("prefill")
+    pf = p.work_items(0)
+    assert len(pf) == 1280 and (pf[:, 3] <= 128).all()   # g = 1: 128 tokens per tile
+    check_cover(b, p)
+    b, p = plan_of("prefill", prefill_block_waves=8)
+    assert len(p.work_items(0)) == 640
+    check_cover(b, p)
+    b, p = plan_of("prefill", lengths=([300, 600], [300, 5000]))
+    assert (p.work_items(0)[:, 3] > 128).any()            # 5000 cached keys: 256-row tiles
+    b, p = plan_of("prefill", lengths=([300, 600], [300, 5000]), prefill_block_waves=4)
+    assert (p.work_items(0)[:, 3] <= 128).all()
+    check_cover(b, p)
+    b, p = plan_of("mixed", prefill_block_waves=4)         # decode rows in the launch
+    assert (p.work_items(0)[:, 3] * 4 > 128).any()
+    check_cover(b, p)
+    with pytest.raises(pd.PdError):
+        plan_of("prefill", prefill_block_waves=2)
+
+
 @pytest.mark.parametrize("chunk", [2_147_483_647, 2_147_483_000, 2_147_483_616, 1 << 30, 40, 31])
 def test_decode_chunk_option_near_int32_max_still_covers_every_row(chunk):
     """A decode_chunk_keys option near INT32_MAX is clamped, not wrapped: the
