@@ -112,18 +112,23 @@ def algorithmic_work(b, elt=2):
 def measured_traffic(workload):
     """HBM bytes per attention launch from the committed PMC summary
     (FETCH_SIZE and WRITE_SIZE runs, calibrated on the pack kernel's known
-    copy size), or None when the kernel source changed since the counters
-    were taken (the summary records the source hash)."""
+    copy size), or None when the kernels or the planner (which decides the
+    launch's blocks and their order) changed since the counters were taken:
+    the summary records both sources' hashes."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "attention_long_pmc_traffic.txt")
-    src = os.path.join(ROOT, "decode_attention_kv_pd_amd", "csrc", "attention.hip")
+    csrc = os.path.join(ROOT, "decode_attention_kv_pd_amd", "csrc")
     if workload != "long" or not os.path.exists(path):
         return None
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+    def digest(name):
+        return hashlib.sha256(open(os.path.join(csrc, name), "rb").read()).hexdigest()[:16]
+
+    want = {"attention_sha256_16": digest("attention.hip"), "planner_sha256_16": digest("api.cpp")}
     for line in open(path):
         if line.startswith("TRAFFIC "):
             kv = dict(t.split("=", 1) for t in line.split()[1:])
-            if kv.get("attention_sha256_16") == digest:
+            if all(kv.get(k) == v for k, v in want.items()):
                 return int(kv["bytes_per_launch"])
     return None
 

@@ -204,6 +204,13 @@ int equal_chunk_len(int32_t kv, int chunk) {
   return (int)std::min<int64_t>(round_up32(((int64_t)kv + nch - 1) / nch), (int64_t)1 << 30);
 }
 
+// Length of the equal chunks of kv keys whose count is the nearest to
+// kv / target (at least one), rounded up to a multiple of 32.
+int nearest_chunk_len(int32_t kv, int target) {
+  const int64_t nch = std::max<int64_t>(1, ((int64_t)kv + target / 2) / target);
+  return (int)std::min<int64_t>(round_up32(((int64_t)kv + nch - 1) / nch), (int64_t)1 << 30);
+}
+
 // ---- decode role planning.
 // A (request, KV head) whose qo * g query rows fit kMaxDecodeRows is a decode
 // row group.  Rows <= 16: one wavefront with one 16-row column group; <= 32:
@@ -216,9 +223,19 @@ int equal_chunk_len(int32_t kv, int chunk) {
 //     spans, one per queue, so every queue streams the same number of keys
 //     and changes row group (reloading its Q) only where a span crosses a
 //     group boundary.
-//   * Many prefill tiles: every group is cut into equal chunks of about
-//     decode_chunk_keys, each its own queue, and the decode blocks
-//     interleave with the prefill tiles.
+//   * Many prefill tiles: every group is cut into equal chunks, each its own
+//     queue, and the decode blocks interleave with the prefill tiles.  The
+//     chunk is sized so that a decode block (eight chunks) lasts about as
+//     long as the launch's mean prefill tile: the hardware dispatches blocks
+//     in order, one XCD after the other, so blocks of very unequal length
+//     leave CUs idle mid-launch and a tail at its end.  The two durations
+//     are priced with the per-CU rates measured for this mix on MI355X: a
+//     decode block streams 37.7-40 GB/s beside prefill tiles whatever its
+//     length, a prefill tile runs 4.3 TFLOP/s.  (Long mixed workload, 2048
+//     tiles of 3.8 GFLOP: 2 / 3 / 4 / 5 / 6 / 8 chunks per 32768-key group
+//     ran 11.45-11.87 / 12.04 / 10.68-11.10 / 11.20 / 11.68 / 12.1 ms on the
+//     same boxes, with 10 / 13 / 3 / 6.5 / - / 20 % of CU time idle.)
+//     decode_chunk_keys > 0 sets the chunk instead.
 // Partial results: piece i of a group of `rows` rows owns the partial rows
 // [part0 + i rows, part0 + (i + 1) rows).
 struct DecodeGroup {
@@ -229,9 +246,11 @@ struct DecodeGroup {
 constexpr int kClsWidth[3] = {1, 1, 2};  // wavefronts per queue
 constexpr int kClsNcg[3] = {1, 2, 2};    // 16-row column groups per wavefront
 constexpr int kMinSpanKeys = 256;        // shortest span worth a queue
+constexpr double kMixDecodeBytesPerCu = 38.5e9;   // B/s of one CU's decode block beside prefill tiles
+constexpr double kMixPrefillFlopsPerCu = 4.3e12;  // flop/s of one CU's prefill tile in the same launch
 
 pd_status build_decode(pd_plan_s& P, const pd_plan_options* opts, int num_cus, int n_prefill_tiles,
-                       std::vector<double>& block_cost) {
+                       double mean_tile_flops, std::vector<double>& block_cost) {
   const pd_attn_desc& d = P.desc;
   const int g = P.g, H_kv = d.num_kv_heads, D = d.head_dim, elt = elt_bytes(&d);
   std::vector<DecodeGroup> groups;
@@ -291,20 +310,21 @@ pd_status build_decode(pd_plan_s& P, const pd_plan_options* opts, int num_cus, i
       }
     }
   } else {
+    const bool forced = opts && opts->decode_chunk_keys > 0;
     int chunk;
-    if (opts && opts->decode_chunk_keys > 0) {
+    if (forced) {
       chunk = clamp_chunk_option(opts->decode_chunk_keys, P);
     } else {
-      const int64_t target_units = (int64_t)num_cus * 16;
-      int64_t c = (wave_keys + target_units - 1) / target_units;
-      c = (c + 255) / 256 * 256;
-      chunk = (int)std::min<int64_t>(std::max<int64_t>(c, 256), 16384);
+      // keys of a chunk whose block of kWavesPerBlock chunks lasts one mean prefill tile
+      const double block_bytes = mean_tile_flops / kMixPrefillFlopsPerCu * kMixDecodeBytesPerCu;
+      const double c = block_bytes / pdk::kWavesPerBlock / (2.0 * D * elt);
+      chunk = (int)std::min(std::max(c, 256.0), 16384.0);
     }
-    P.chunk_keys = chunk;
+    P.chunk_keys = forced ? chunk : 0;  // else: the longest unit, below
     for (size_t gi = 0; gi < groups.size(); ++gi) {
       DecodeGroup& gr = groups[gi];
       const int kv = P.req[gr.r].kv;
-      const int len = equal_chunk_len(kv, chunk);
+      const int len = forced ? equal_chunk_len(kv, chunk) : nearest_chunk_len(kv, chunk);
       for (int64_t k0 = 0; k0 < kv; k0 += len) {
         gr.pieces.push_back({(int)k0, (int)std::min<int64_t>(kv, k0 + len)});
         queues[gr.cls].push_back({{(int)gi, (int)gr.pieces.size() - 1}});
@@ -445,7 +465,10 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   // ---- decode units: (request, KV head) row groups of at most kMaxDecodeRows
   // query rows, each cut into key chunks; units go to per-wavefront queues
   std::vector<double> db_cost;
-  pd_status ds = build_decode(P, opts, num_cus, (int)P.pf.size(), db_cost);
+  double pf_flops = 0;
+  for (double c : pf_cost) pf_flops += c;
+  pd_status ds = build_decode(P, opts, num_cus, (int)P.pf.size(),
+                              pf_cost.empty() ? 0.0 : pf_flops / (double)pf_cost.size(), db_cost);
   if (ds != PD_OK) return ds;
   const int n_db = (int)db_cost.size();
 
