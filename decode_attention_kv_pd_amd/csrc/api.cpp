@@ -248,9 +248,10 @@ constexpr int kClsNcg[3] = {1, 2, 2};    // 16-row column groups per wavefront
 constexpr int kMinSpanKeys = 256;        // shortest span worth a queue
 constexpr double kMixDecodeBytesPerCu = 38.5e9;   // B/s of one CU's decode block beside prefill tiles
 constexpr double kMixPrefillFlopsPerCu = 4.3e12;  // flop/s of one CU's prefill tile in the same launch
+constexpr double kStreamBytesPerS = 6.5e12;       // streaming reads of the whole chip (MI355X, measured)
 
 pd_status build_decode(pd_plan_s& P, const pd_plan_options* opts, int num_cus, int n_prefill_tiles,
-                       double mean_tile_flops, std::vector<double>& block_cost) {
+                       double mean_tile_flops, double max_tile_flops, std::vector<double>& block_cost) {
   const pd_attn_desc& d = P.desc;
   const int g = P.g, H_kv = d.num_kv_heads, D = d.head_dim, elt = elt_bytes(&d);
   std::vector<DecodeGroup> groups;
@@ -273,7 +274,15 @@ pd_status build_decode(pd_plan_s& P, const pd_plan_options* opts, int num_cus, i
     int grp, piece;
   };
   std::vector<std::vector<QEntry>> queues[3];
-  const bool one_round = n_prefill_tiles < num_cus && !(opts && opts->decode_chunk_keys > 0);
+  // One round of queues on the CUs the prefill tiles leave, unless that
+  // round would outlast the longest prefill tile (its CUs would then idle
+  // while the decode queues finish): then chunks interleaved with the tiles.
+  bool one_round = n_prefill_tiles < num_cus && !(opts && opts->decode_chunk_keys > 0);
+  if (one_round && n_prefill_tiles > 0) {
+    const int free_cus = std::max(num_cus - n_prefill_tiles, num_cus / 2);
+    const double round_s = (double)P.decode_bytes / std::min(free_cus * kMixDecodeBytesPerCu, kStreamBytesPerS);
+    one_round = round_s <= max_tile_flops / kMixPrefillFlopsPerCu;
+  }
   if (one_round) {
     const int slots =
         pdk::kWavesPerBlock * (n_prefill_tiles == 0 ? num_cus : std::max(num_cus - n_prefill_tiles, num_cus / 2));
@@ -465,10 +474,10 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   // ---- decode units: (request, KV head) row groups of at most kMaxDecodeRows
   // query rows, each cut into key chunks; units go to per-wavefront queues
   std::vector<double> db_cost;
-  double pf_flops = 0;
-  for (double c : pf_cost) pf_flops += c;
+  double pf_flops = 0, pf_max = 0;
+  for (double c : pf_cost) pf_flops += c, pf_max = std::max(pf_max, c);
   pd_status ds = build_decode(P, opts, num_cus, (int)P.pf.size(),
-                              pf_cost.empty() ? 0.0 : pf_flops / (double)pf_cost.size(), db_cost);
+                              pf_cost.empty() ? 0.0 : pf_flops / (double)pf_cost.size(), pf_max, db_cost);
   if (ds != PD_OK) return ds;
   const int n_db = (int)db_cost.size();
 

@@ -372,6 +372,36 @@ def test_block_map_covers_work_and_keeps_xcd_affinity(order):
         assert (bmap[:len(pf)] >= 0).all()
 
 
+def test_decode_chunks_of_mixed_launches():
+    """Mixed launches: with a prefill tile per CU or more, decode groups are
+    cut into chunks whose block of eight streams about as long as the mean
+    prefill tile runs (the long workload: four 8192-key chunks per group,
+    1024 decode blocks), one chunk per queue; with fewer tiles the decode
+    runs in one round of queues on the free CUs unless that round would
+    outlast the longest tile (the mixed workload's 63 decodes on 128 CUs
+    would: chunks), and a small decode batch beside a 128-token prompt keeps
+    its one round (queues of several pieces)."""
+    def plan_of(b):
+        d = pd.make_desc(b.H_q, b.H_kv, b.D, b.ps, b.dtype, b.causal)
+        return pd.pd_plan(d, b.qo_lens, b.kv_lens, b.page_indptr, b.page_indices, b.num_pool_pages)
+    b = make_batch("long", materialize=False)
+    p = plan_of(b)
+    du, dq, bmap = p.work_items(1), p.work_items(4)[:, 0], p.work_items(3)[:, 0]
+    assert set((du[:, 3] - du[:, 2]).tolist()) == {8192} and (np.diff(dq) == 1).all()
+    assert (bmap < 0).sum() == 1024
+    check_cover(b, p)
+    b = make_batch("mixed", materialize=False)
+    p = plan_of(b)
+    du, dq = p.work_items(1), p.work_items(4)[:, 0]
+    assert (np.diff(dq) == 1).all() and (du[:, 3] - du[:, 2]).max() <= 512
+    check_cover(b, p)
+    b = make_batch("mixed", materialize=False, lengths=([128] + [1] * 32, [128] * 33))
+    p = plan_of(b)
+    dq = p.work_items(4)[:, 0]
+    assert np.diff(dq).max() > 1
+    check_cover(b, p)
+
+
 def test_prefill_block_shape_for_short_prompts():
     """Prefill-only launches of short caches run 128-row tiles (4-wavefront
     blocks, two per CU); 8 keeps 256-row tiles; a launch with decode rows,
