@@ -532,7 +532,7 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
   P.off_du = off;
   off = align_up(off + sizeof(pdk::DecodeUnit) * P.du.size());
   P.off_mg = off;
-  off = align_up(off + sizeof(pdk::MergeGroup) * P.mg.size());
+  off = align_up(off + sizeof(pdk::MergeRec) * P.mg.size());
   P.off_rows = off;
   off = align_up(off + sizeof(int32_t) * 2 * (size_t)P.total_rows);
   P.meta_bytes = off;
@@ -569,7 +569,14 @@ pd_status build_plan(pd_plan_s& P, const pd_plan_options* opts) {
     pdk::DecodeUnit* du = (pdk::DecodeUnit*)(P.blob.data() + P.off_du);
     for (size_t i = 0; i < P.du.size(); ++i) du[i] = {P.du[i], P.req[P.du[i].req]};
   }
-  put(P.off_mg, P.mg.data(), sizeof(pdk::MergeGroup) * P.mg.size());
+  {
+    pdk::MergeRec* mr = (pdk::MergeRec*)(P.blob.data() + P.off_mg);
+    for (size_t i = 0; i < P.mg.size(); ++i) {
+      const pdk::MergeGroup& m = P.mg[i];
+      const pdk::ReqInfo& ri = P.req[m.req];
+      mr[i] = {m.part0, m.nparts, ri.qo * P.g, ri.qo_start, m.hk, 0, 0, 0};
+    }
+  }
   {
     int32_t* rp = (int32_t*)(P.blob.data() + P.off_rows);
     for (int r = 0; r < P.B; ++r) {
@@ -636,7 +643,7 @@ pdk::AttnParams attn_params(const pd_plan_s& P, void* d_ws) {
   a.page_indices = (const int32_t*)(ws + P.off_pages);
   a.launch = (const pdk::LaunchRec*)(ws + P.off_launch);
   a.du = (const pdk::DecodeUnit*)(ws + P.off_du);
-  a.mg = (const pdk::MergeGroup*)(ws + P.off_mg);
+  a.mg = (const pdk::MergeRec*)(ws + P.off_mg);
   a.n_blocks = (int32_t)P.block_map.size();
   a.prefill4 = P.prefill4 ? 1 : 0;
   a.part_o = (float*)(ws + P.off_part_o);

@@ -1164,11 +1164,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(AttnParams p) {
 // w_i = exp(lse_i - LSE*), O = sum_i w_i o_i / sum_i w_i,
 // LSE = LSE* + ln sum_i w_i; parts are visited in a fixed order.
 // ------------------------------------------------------------------------
+// Groups of at most kMergeBatch parts load every part's LSE and output at
+// once (one round trip), then combine them in part order; larger groups
+// take two passes over the parts.  Both orders of arithmetic are the same.
+constexpr int kMergeBatch = 8;
+
 template <int D>
 __global__ __launch_bounds__(kBlockThreads) void merge_kernel(AttnParams p) {
-  const MergeGroup mg = ldc(p.mg + blockIdx.x);
-  const ReqInfo ri = ldc(p.req + mg.req);
-  const int nrows = ri.qo * p.g;
+  const MergeRec mg = ldc(p.mg + blockIdx.x);
+  const int nrows = mg.nrows;
   constexpr int D4 = D / 4;
   for (int idx = threadIdx.x; idx < nrows * D4; idx += kBlockThreads) {
     const int n = idx / D4, d4 = idx % D4;
@@ -1176,18 +1180,39 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(AttnParams p) {
     const int64_t base = (int64_t)mg.part0 + n;
     const int64_t stride = nrows;  // chunk i + 1 is nrows partial rows further
     float mx = -INFINITY;
-    for (int i = 0; i < mg.nparts; ++i) mx = fmaxf(mx, p.part_lse[base + i * stride]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float sw = 0.f;
-    for (int i = 0; i < mg.nparts; ++i) {
-      const int64_t slot = base + i * stride;
-      const float li = p.part_lse[slot];
-      const float wi = (li == -INFINITY) ? 0.f : __expf(li - mx);
-      const f32x4 oi = *(const f32x4*)(p.part_o + slot * D + 4 * d4);
-      acc += oi * wi;
-      sw += wi;
+    if (mg.nparts <= kMergeBatch) {
+      float l[kMergeBatch];
+      f32x4 o[kMergeBatch];
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const int64_t slot = base + (int64_t)min(i, mg.nparts - 1) * stride;
+        l[i] = p.part_lse[slot];
+        o[i] = *(const f32x4*)(p.part_o + slot * D + 4 * d4);
+      }
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i)
+        if (i < mg.nparts) mx = fmaxf(mx, l[i]);
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i)
+        if (i < mg.nparts) {
+          const float wi = (l[i] == -INFINITY) ? 0.f : __expf(l[i] - mx);
+          acc += o[i] * wi;
+          sw += wi;
+        }
+    } else {
+      for (int i = 0; i < mg.nparts; ++i) mx = fmaxf(mx, p.part_lse[base + i * stride]);
+      for (int i = 0; i < mg.nparts; ++i) {
+        const int64_t slot = base + i * stride;
+        const float li = p.part_lse[slot];
+        const float wi = (li == -INFINITY) ? 0.f : __expf(li - mx);
+        const f32x4 oi = *(const f32x4*)(p.part_o + slot * D + 4 * d4);
+        acc += oi * wi;
+        sw += wi;
+      }
     }
-    const int64_t row = (int64_t)(ri.qo_start + t) * p.H_q + h;
+    const int64_t row = (int64_t)(mg.qo_start + t) * p.H_q + h;
     *(f32x4*)(p.out + row * D + 4 * d4) = acc * (1.f / sw);
     if (d4 == 0 && p.lse) p.lse[row] = mx + __logf(sw);
   }

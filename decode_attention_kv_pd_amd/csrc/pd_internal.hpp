@@ -61,6 +61,14 @@ struct MergeGroup {
   int32_t req, hk, part0, nparts;
 };
 
+// What the merge kernel reads for one row group, 32 bytes: its partial rows
+// (chunk i's row n at part0 + i * nrows + n) and where its rows go (row n:
+// token qo_start + n / g, head hk * g + n % g), so that the group's first
+// loads depend on this record only.
+struct MergeRec {
+  int32_t part0, nparts, nrows, qo_start, hk, rsv0, rsv1, rsv2;
+};
+
 constexpr int kBlockThreads = 256;  // append, pack, merge and the fp32 kernel
 constexpr int kAttnWaves = 8;       // wavefronts per block of the bf16 attention kernel
 constexpr int kAttnThreads = 64 * kAttnWaves;
@@ -79,7 +87,7 @@ struct AttnParams {
   const int32_t* page_indices;
   const LaunchRec* launch;  // one record per block of the attention launch
   const DecodeUnit* du;     // decode units in queue order
-  const MergeGroup* mg;
+  const MergeRec* mg;
   float* part_o;    // [partial rows][D]
   float* part_lse;  // [partial rows]
   int32_t n_pf, n_du, n_mg, B;
