@@ -105,11 +105,15 @@ typedef struct pd_attn_desc {
 
 /* Optional planner controls (NULL = defaults).
  *   decode_chunk_keys  0 (default): when the launch has fewer prefill tiles
- *                      than compute units, the decode row groups are laid
- *                      end to end and cut into equal spans of keys, one per
- *                      wavefront queue (a queue holds the units its span
- *                      crosses); otherwise each group is cut into equal
- *                      chunks of a length the planner picks, one unit each.
+ *                      than compute units and one round of queues on the
+ *                      CUs they leave free would end within the longest
+ *                      prefill tile (priced at measured MI355X rates), the
+ *                      decode row groups are laid end to end and cut into
+ *                      equal spans of keys, one per wavefront queue (a
+ *                      queue holds the units its span crosses); otherwise
+ *                      each group is cut into equal chunks, one unit each,
+ *                      sized so that a block of eight chunks lasts about
+ *                      as long as the launch's mean prefill tile.
  *                      > 0: every group is cut into chunks of about this
  *                      many keys (rounded up to 32, at most the longest
  *                      cache), one unit per queue
@@ -143,8 +147,8 @@ typedef struct pd_plan_stats {
   int32_t prefill_tiles;       /* MFMA query tiles (rows of prefill requests) */
   int32_t decode_units;        /* split-KV units */
   int32_t decode_row_groups;   /* (request, kv head) groups merged */
-  int32_t decode_chunk_keys;   /* chunk length used (span planning: the
-                                  longest unit) */
+  int32_t decode_chunk_keys;   /* the decode_chunk_keys option as applied,
+                                  else the longest decode unit */
   int64_t prefill_flops;       /* 4 * head_dim * H_q * visible (query, key)
                                   pairs of the prefill rows (algorithmic) */
   int64_t decode_kv_bytes;     /* K + V bytes the decode rows read */
