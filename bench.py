@@ -78,6 +78,10 @@ def parse():
                     help="skip the interference / chunked-prefill sweep")
     ap.add_argument("--sweep-decodes", type=int, default=32, help="decodes in the 1PnD sweep batches")
     ap.add_argument("--no-mla", action="store_true", help="skip the latent-cache (MLA) decode legs")
+    ap.add_argument("--loop", choices=("prefill", "decode", "mixed"), default=None,
+                    help="only run one attention launch kind of the workload back to back for "
+                         "--loop-seconds (for sampling board power and clocks from another process)")
+    ap.add_argument("--loop-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-workers", type=int, default=0,
                     help="oracle processes (0: the host's available cores, at most 16)")
     ap.add_argument("--cpu-decode-rows", type=int, default=8, help="decode rows per oracle process")
@@ -639,6 +643,27 @@ def mla_legs(args, pd, torch, meter):
     return res
 
 
+def power_loop(args, pd, torch, b, desc, pool, q):
+    """--loop: one launch kind (prefill-only, decode-only or the mixed launch)
+    back to back for --loop-seconds, so that the board's power and clocks
+    can be read meanwhile (e.g. `amd-smi metric -p -c`); prints one JSON line
+    with the launches and their mean time."""
+    dec = b.qo_lens == 1
+    sel = {"prefill": ~dec, "decode": dec, "mixed": np.ones(b.B, bool)}[args.loop]
+    p, wsp, qs, o, ls = sub_plan(pd, torch, b, desc, sel, q)
+    torch.cuda.synchronize()
+    print(f"[bench] {args.loop} launches back to back for {args.loop_seconds} s", file=sys.stderr, flush=True)
+    n, t0 = 0, time.time()
+    while time.time() - t0 < args.loop_seconds:
+        for _ in range(20):
+            pd.pd_attention_run(p, wsp, qs, pool, o, ls)
+        torch.cuda.synchronize()
+        n += 20
+    dt = time.time() - t0
+    print(json.dumps({"loop": args.loop, "launches": n, "seconds": round(dt, 2),
+                      "ms_per_launch": round(dt / n * 1e3, 4)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -662,6 +687,8 @@ def main():
     # ---- device-resident inputs
     t = device_inputs(torch, b, pd)
     pool, q, k_new, v_new, out, lse = (t[k] for k in ("pool", "q", "k_new", "v_new", "out", "lse"))
+    if args.loop:
+        return power_loop(args, pd, torch, b, desc, pool, q)
     r_pack = int(np.argmax(b.qo_lens))
     pack_ids = b.request_pages(r_pack)
     unpack_ids = np.random.default_rng(7).permutation(b.spare_pages)[:len(pack_ids)].astype(np.int32)
