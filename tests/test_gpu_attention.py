@@ -271,6 +271,27 @@ def test_chunked_prefill_equals_full():
     assert np.abs(got - out_f).max() <= 2 * tolerance(full)
 
 
+@pytest.mark.parametrize("cus", [16, 64])
+def test_mixed_launch_chunked_decode(cus):
+    """A prompt with a prefill tile per CU or more beside decodes of 1, 5
+    and 9 tokens (16-row, 32-row and paired 64-row groups at g = 4): the
+    decode groups are cut into chunks sized to the prefill tiles (many
+    pieces per group, a ragged last piece) and interleaved with the tiles;
+    every row at parity."""
+    qo = [512, 1, 1, 5, 1, 9, 1, 1, 1]
+    kv = [512, 3000, 5000, 700, 1500, 4100, 257, 33, 2049]
+    b = batch("mixed", (tuple(qo), tuple(kv)))
+    run = DeviceRun(b, num_cus=cus)
+    dq = run.plan.work_items(4)[:, 0]
+    assert (np.diff(dq) == 1).all() and len(dq) > 100        # one chunk per queue, many chunks
+    print(f"case chunked_{cus}: {len(dq) - 1} decode units", flush=True)
+    out, lse = run.step()
+    O, L = oracle_outputs(b)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    assert report(f"chunked_{cus}", out, O) <= tolerance(b)
+    assert np.abs(lse - L).max() <= lse_tol(b) + 2.0 ** -20 * np.abs(L).max()
+
+
 @pytest.mark.parametrize("L", [128, 1024])
 def test_interference_sweep_batches(L):
     """The interference sweep's 1PnD batch (one causal prompt of L tokens
