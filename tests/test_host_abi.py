@@ -375,8 +375,9 @@ def test_block_map_covers_work_and_keeps_xcd_affinity(order):
 def test_decode_chunks_of_mixed_launches():
     """Mixed launches: with a prefill tile per CU or more, decode groups are
     cut into chunks whose block of eight streams about as long as the mean
-    prefill tile runs (the long workload: four 8192-key chunks per group,
-    1024 decode blocks), one chunk per queue; with fewer tiles the decode
+    prefill tile runs (the long workload: four chunks per group graded
+    about 8192 keys, longest first, 1024 decode blocks), one chunk per
+    queue, queues longest first; with fewer tiles the decode
     runs in one round of queues on the free CUs unless that round would
     outlast the longest tile (the mixed workload's 63 decodes on 128 CUs
     would: chunks), and a small decode batch beside a 128-token prompt keeps
@@ -387,8 +388,14 @@ def test_decode_chunks_of_mixed_launches():
     b = make_batch("long", materialize=False)
     p = plan_of(b)
     du, dq, bmap = p.work_items(1), p.work_items(4)[:, 0], p.work_items(3)[:, 0]
-    assert set((du[:, 3] - du[:, 2]).tolist()) == {8192} and (np.diff(dq) == 1).all()
-    assert (bmap < 0).sum() == 1024
+    n = du[:, 3] - du[:, 2]
+    assert (np.diff(dq) == 1).all() and (bmap < 0).sum() == 1024
+    assert len(set(n.tolist())) == 4 and (abs(n - 8192) <= 0.1 * 8192).all()
+    assert (np.diff(n) <= 0).all()                                   # longest first
+    for r, hk in {(int(a), int(c)) for a, c in du[:, :2]}:
+        pieces = sorted(du[(du[:, 0] == r) & (du[:, 1] == hk), 2:4].tolist())
+        assert len(pieces) == 4 and pieces[0][0] == 0 and pieces[-1][1] == int(b.kv_lens[r])
+        assert [q[1] - q[0] for q in pieces] == sorted([q[1] - q[0] for q in pieces], reverse=True)
     check_cover(b, p)
     b = make_batch("mixed", materialize=False)
     p = plan_of(b)
