@@ -223,7 +223,7 @@ int nearest_chunk_len(int32_t kv, int target) {
 //     spans, one per queue, so every queue streams the same number of keys
 //     and changes row group (reloading its Q) only where a span crosses a
 //     group boundary.
-//   * Many prefill tiles: every group is cut into equal chunks, each its own
+//   * Many prefill tiles: every group is cut into chunks, each its own
 //     queue, and the decode blocks interleave with the prefill tiles.  The
 //     chunk is sized so that a decode block (eight chunks) lasts about as
 //     long as the launch's mean prefill tile: the hardware dispatches blocks
