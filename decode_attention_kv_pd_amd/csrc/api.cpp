@@ -824,7 +824,7 @@ pd_status build_mla_plan(pd_plan_s& P, const pd_plan_options* opts) {
   P.off_mitems = off;
   off = align_up(off + sizeof(pdk::MlaItem) * P.mitems.size());
   P.off_mmg = off;
-  off = align_up(off + sizeof(pdk::MlaMergeGroup) * P.mmg.size());
+  off = align_up(off + sizeof(pdk::MlaMergeRec) * P.mmg.size());
   P.meta_bytes = off;
   P.off_part_o = off;
   off = align_up(off + sizeof(float) * (size_t)P.n_parts * R * pdk::kMlaLatent);
@@ -839,7 +839,14 @@ pd_status build_mla_plan(pd_plan_s& P, const pd_plan_options* opts) {
   put(P.off_req, P.req.data(), sizeof(pdk::ReqInfo) * P.req.size());
   put(P.off_pages, P.pages.data(), sizeof(int32_t) * P.pages.size());
   put(P.off_mitems, P.mitems.data(), sizeof(pdk::MlaItem) * P.mitems.size());
-  put(P.off_mmg, P.mmg.data(), sizeof(pdk::MlaMergeGroup) * P.mmg.size());
+  {
+    pdk::MlaMergeRec* mr = (pdk::MlaMergeRec*)(P.blob.data() + P.off_mmg);
+    for (size_t i = 0; i < P.mmg.size(); ++i) {
+      const pdk::MlaMergeGroup& m = P.mmg[i];
+      const pdk::ReqInfo& ri = P.req[m.req];
+      mr[i] = {m.part0, m.nparts, m.rg, ri.qo * P.mdesc.num_qo_heads, ri.qo_start, 0, 0, 0};
+    }
+  }
   return PD_OK;
 }
 
@@ -850,7 +857,7 @@ pdk::MlaParams mla_params(const pd_plan_s& P, void* d_ws) {
   a.req = (const pdk::ReqInfo*)(ws + P.off_req);
   a.page_indices = (const int32_t*)(ws + P.off_pages);
   a.items = (const pdk::MlaItem*)(ws + P.off_mitems);
-  a.mg = (const pdk::MlaMergeGroup*)(ws + P.off_mmg);
+  a.mg = (const pdk::MlaMergeRec*)(ws + P.off_mmg);
   a.part_o = (float*)(ws + P.off_part_o);
   a.part_lse = (float*)(ws + P.off_part_lse);
   a.n_items = (int32_t)P.mitems.size();

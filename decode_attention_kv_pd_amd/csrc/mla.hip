@@ -255,31 +255,59 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaParams p) {
 
 // Log-sum-exp merge of split partial results: one wavefront per query row
 // of a merge group (lanes over the 512 latent entries, 8 each), parts in
-// slot order (deterministic for a fixed plan).
+// slot order (deterministic for a fixed plan).  A group of at most
+// kMlaMergeBatch parts loads every part's LSE and output at once (one round
+// trip), then combines them in slot order; larger groups take two passes.
+// Both orders of arithmetic are the same.
+constexpr int kMlaMergeBatch = 8;
+
 __global__ __launch_bounds__(64 * kMlaMergeWaves) void mla_merge_kernel(MlaParams p) {
   const int wg = blockIdx.x * kMlaMergeWaves + uniform_i(threadIdx.x >> 6);
   const int R = p.rows;
   const int gi = wg / R, n = wg % R;
   if (gi >= p.n_mg) return;
-  const MlaMergeGroup mg = ldc(p.mg + gi);
-  const ReqInfo ri = ldc(p.req + mg.req);
+  const MlaMergeRec mg = ldc(p.mg + gi);
   const int rn = R * mg.rg + n;  // row of the request (token rn / H, head rn % H)
-  if (rn >= ri.qo * p.H) return;
+  if (rn >= mg.qo_rows) return;
   const int lane = threadIdx.x & 63;
   float mx = -INFINITY;
-  for (int i = 0; i < mg.nparts; ++i) mx = fmaxf(mx, ldc(p.part_lse + (int64_t)(mg.part0 + i) * R + n));
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
   float sw = 0.f;
-  for (int i = 0; i < mg.nparts; ++i) {
-    const int64_t slot = (int64_t)(mg.part0 + i) * R + n;
-    const float li = ldc(p.part_lse + slot);
-    const float wi = (li == -INFINITY) ? 0.f : __expf(li - mx);
-    const float* po = p.part_o + slot * kMlaLatent + 4 * lane;
-    a0 += *(const f32x4*)po * wi;
-    a1 += *(const f32x4*)(po + 256) * wi;
-    sw += wi;
+  if (mg.nparts <= kMlaMergeBatch) {
+    float l[kMlaMergeBatch];
+    f32x4 o0[kMlaMergeBatch], o1[kMlaMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMlaMergeBatch; ++i) {
+      const int64_t slot = (int64_t)(mg.part0 + min(i, mg.nparts - 1)) * R + n;
+      l[i] = ldc(p.part_lse + slot);
+      const float* po = p.part_o + slot * kMlaLatent + 4 * lane;
+      o0[i] = *(const f32x4*)po;
+      o1[i] = *(const f32x4*)(po + 256);
+    }
+#pragma unroll
+    for (int i = 0; i < kMlaMergeBatch; ++i)
+      if (i < mg.nparts) mx = fmaxf(mx, l[i]);
+#pragma unroll
+    for (int i = 0; i < kMlaMergeBatch; ++i)
+      if (i < mg.nparts) {
+        const float wi = (l[i] == -INFINITY) ? 0.f : __expf(l[i] - mx);
+        a0 += o0[i] * wi;
+        a1 += o1[i] * wi;
+        sw += wi;
+      }
+  } else {
+    for (int i = 0; i < mg.nparts; ++i) mx = fmaxf(mx, ldc(p.part_lse + (int64_t)(mg.part0 + i) * R + n));
+    for (int i = 0; i < mg.nparts; ++i) {
+      const int64_t slot = (int64_t)(mg.part0 + i) * R + n;
+      const float li = ldc(p.part_lse + slot);
+      const float wi = (li == -INFINITY) ? 0.f : __expf(li - mx);
+      const float* po = p.part_o + slot * kMlaLatent + 4 * lane;
+      a0 += *(const f32x4*)po * wi;
+      a1 += *(const f32x4*)(po + 256) * wi;
+      sw += wi;
+    }
   }
-  const int64_t row = (int64_t)(ri.qo_start + rn / p.H) * p.H + rn % p.H;
+  const int64_t row = (int64_t)(mg.qo_start + rn / p.H) * p.H + rn % p.H;
   const float inv = 1.f / sw;
   *(f32x4*)(p.out + row * kMlaLatent + 4 * lane) = a0 * inv;
   *(f32x4*)(p.out + row * kMlaLatent + 256 + 4 * lane) = a1 * inv;

@@ -152,6 +152,14 @@ struct MlaMergeGroup {
   int32_t req, rg, part0, nparts;
 };
 
+// What the MLA merge kernel reads for one (request, row group), 32 bytes:
+// its partial slots and where the group's rows go (row R rg + n of the
+// request, if below qo_rows = qo * H, is token qo_start + that row / H), so
+// that its first loads depend on this record only.
+struct MlaMergeRec {
+  int32_t part0, nparts, rg, qo_rows, qo_start, rsv0, rsv1, rsv2;
+};
+
 struct MlaParams {
   const void* q;      // [rows][H][kMlaWidth] bf16
   const void* pool;   // [pages][ps][kMlaWidth] bf16
@@ -161,7 +169,7 @@ struct MlaParams {
   const ReqInfo* req;
   const int32_t* page_indices;
   const MlaItem* items;
-  const MlaMergeGroup* mg;
+  const MlaMergeRec* mg;
   float* part_o;      // [n_parts][rows][kMlaLatent]
   float* part_lse;    // [n_parts][rows]
   int32_t n_items, n_mg, B, total_rows;
