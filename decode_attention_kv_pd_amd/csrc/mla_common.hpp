@@ -47,12 +47,45 @@ __device__ __forceinline__ int mla_page(const MlaParams& p, const ReqInfo& ri, i
   return ldc(p.page_indices + ri.page_start + (min(key, ri.kv - 1) >> p.ps_shift));
 }
 
+// A step whose 32 keys are all valid: keys b .. b + 15 are consecutive
+// slots of page pgA and b + 16 .. b + 31 of page pgB (pages hold >= 16
+// aligned keys), so each of its loads is a wave-uniform base plus a
+// loop-invariant lane offset (the scalar-base form of the load).
+struct MlaFullStep {
+  const char* baseA;  // cache row of key b
+  const char* baseB;  // cache row of key b + 16
+  LDS_AS char* st;    // stage
+};
+__device__ __forceinline__ MlaFullStep mla_full_step(const MlaParams& p, int b, int pgA, int pgB, LDS_AS char* st) {
+  constexpr int64_t RB = 2 * kMlaWidth;  // bytes per cache row
+  const char* pool = (const char*)p.pool;
+  const int psm = p.ps - 1;
+  return {pool + ((int64_t)pgA * p.ps + (b & psm)) * RB, pool + ((int64_t)pgB * p.ps + ((b + 16) & psm)) * RB, st};
+}
+
+// Load I (0..8) of wavefront w's share of a full step: I < 8 the latent
+// load (tile I / 2, rows 4 (w + 4 (I % 2)) .. +3), I = 8 the rotary load
+// (rows 8 w .. +7).  The loads can be issued one at a time.
+template <int I>
+__device__ __forceinline__ void mla_issue_full(const MlaFullStep& f, int w, int lane) {
+  constexpr int64_t RB = 2 * kMlaWidth;
+  if constexpr (I < 8) {
+    constexpr int q4 = I / 2;
+    const int jb = w + 4 * (I % 2);
+    const uint32_t off = (4 * w + Lds<128>::dma_row(lane)) * RB + 256 * q4 + 16 * Lds<128>::dma_chunk(lane);
+    load_lds16_sbase(I % 2 ? f.baseB : f.baseA, off, f.st + q4 * MlaCfg::QUARTER + jb * Lds<128>::BLOCK);
+  } else {
+    const uint32_t off = (8 * (w % 2) + Lds<64>::dma_row(lane)) * RB + 2 * kMlaLatent + 16 * Lds<64>::dma_chunk(lane);
+    load_lds16_sbase(w < 2 ? f.baseA : f.baseB, off, f.st + MlaCfg::ROPE + w * Lds<64>::BLOCK);
+  }
+}
+
 // Wavefront w's share (latent loads i = 0..7: tile i / 2, rows 4 (w + 4 (i
 // % 2)) .. +3; then one rotary load, rows 8 w .. +7) of the 36 block loads
 // of the step at key b into stage `st`.  pgA / pgB are the pages of keys b
-// .. b + 15 and b + 16 .. b + 31 (pages hold >= 16 aligned keys).  Keys >=
-// kv (only in a request's last step) are read from key kv - 1 instead:
-// finite data, masked later, and tail slots are never read.
+// .. b + 15 and b + 16 .. b + 31.  Keys >= kv (only in a request's last
+// step) are read from key kv - 1 instead: finite data, masked later, and
+// tail slots are never read.
 __device__ __forceinline__ void mla_issue(const MlaParams& p, const ReqInfo& ri, int b, int pgA, int pgB,
                                           int w, int lane, LDS_AS char* st) {
   const char* pool = (const char*)p.pool;
@@ -60,21 +93,16 @@ __device__ __forceinline__ void mla_issue(const MlaParams& p, const ReqInfo& ri,
   const int psm = p.ps - 1;
   constexpr int64_t RB = 2 * kMlaWidth;  // bytes per cache row
   if (b + 32 <= ri.kv) {
-    // every row valid: keys b .. b + 15 are consecutive slots of page pgA and
-    // b + 16 .. b + 31 of page pgB, so each load is a wave-uniform base plus
-    // a loop-invariant lane offset (the scalar-base form of the load)
-    const char* baseA = pool + ((int64_t)pgA * p.ps + (b & psm)) * RB;
-    const char* baseB = pool + ((int64_t)pgB * p.ps + ((b + 16) & psm)) * RB;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q4 = i / 2, jb = w + 4 * (i % 2);
-      const uint32_t off = (4 * (jb % 4) + Lds<128>::dma_row(lane)) * RB + 256 * q4 + 16 * Lds<128>::dma_chunk(lane);
-      load_lds16_sbase(jb >= 4 ? baseB : baseA, off, st + q4 * MlaCfg::QUARTER + jb * Lds<128>::BLOCK);
-    }
-    {
-      const uint32_t off = (8 * (w % 2) + Lds<64>::dma_row(lane)) * RB + 2 * kMlaLatent + 16 * Lds<64>::dma_chunk(lane);
-      load_lds16_sbase(w < 2 ? baseA : baseB, off, st + MlaCfg::ROPE + w * Lds<64>::BLOCK);
-    }
+    const MlaFullStep f = mla_full_step(p, b, pgA, pgB, st);
+    mla_issue_full<0>(f, w, lane);
+    mla_issue_full<1>(f, w, lane);
+    mla_issue_full<2>(f, w, lane);
+    mla_issue_full<3>(f, w, lane);
+    mla_issue_full<4>(f, w, lane);
+    mla_issue_full<5>(f, w, lane);
+    mla_issue_full<6>(f, w, lane);
+    mla_issue_full<7>(f, w, lane);
+    mla_issue_full<8>(f, w, lane);
     return;
   }
 #pragma unroll

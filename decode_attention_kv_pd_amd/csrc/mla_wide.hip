@@ -146,18 +146,26 @@ constexpr int wide_k_off() {
                              : Lds<64>::chunk_step(R - WideCfg::KS_LAT);
 }
 
-template <int R>
+// LOADS: the wavefront's 9 direct loads of a later full step are issued
+// between the score products (load j after product 4 j + 1) instead of all
+// at once after the barrier: the products form one dependent chain, whose
+// gaps take the issue, and the CU's load path moves the step's 38 KB while
+// the products run.
+template <int R, bool LOADS>
 __device__ __forceinline__ void wide_s_pipe(u32x4 (&kf)[WideCfg::SRING], f32x16& s, const u32x4 (&qf)[WideCfg::KS],
-                                            const LDS_AS char* kl, const LDS_AS char* kr) {
+                                            const LDS_AS char* kl, const LDS_AS char* kr, const MlaFullStep& nx,
+                                            int w, int lane) {
   constexpr int NR = WideCfg::KS, RING = WideCfg::SRING;
   if constexpr (R >= RING) {
     constexpr int i = R - RING;
     lgkm_wait_for<(NR - 1 - i < RING - 1) ? NR - 1 - i : RING - 1>(kf[i % RING]);
     s = mfma32(kf[i % RING], qf[i], s);
+    if constexpr (LOADS && i % 4 == 1 && i / 4 < MlaCfg::LOADS_PER_WAVE) mla_issue_full<i / 4>(nx, w, lane);
   }
   if constexpr (R < NR) kf[R % RING] = lds_read16_asm<wide_k_off<R>()>(R < WideCfg::KS_LAT ? kl : kr);
-  if constexpr (R + 1 < NR + RING) wide_s_pipe<R + 1>(kf, s, qf, kl, kr);
+  if constexpr (R + 1 < NR + RING) wide_s_pipe<R + 1, LOADS>(kf, s, qf, kl, kr, nx, w, lane);
 }
+static_assert(4 * (MlaCfg::LOADS_PER_WAVE - 1) + 1 < WideCfg::KS, "every interleaved load has a product before it");
 
 // Value product m = 16 kk + db: O^T[32 db ..][rows] += V^T[32 db ..][keys of
 // k-step kk] P^T[keys of kk][rows].  Lane (entry 32 db + lane % 32, half h)
@@ -221,14 +229,15 @@ __device__ __forceinline__ float wide_exp(const f32x16& s, float cl, float mc, u
 // s[4 g + e].  Then the speculative online softmax per row (the running
 // reference max m_ref changes only when some weight would reach 2^64), and
 // O^T += V^T P^T.
+template <bool LOADS>
 __device__ __forceinline__ void wide_step(const MlaParams& p, const LDS_AS char* st, int b, int lim, int h2,
                                           int k_lat, int k_rope, int v_off, const u32x4 (&qf)[WideCfg::KS],
-                                          float& m_ref, float& lsum) {
+                                          float& m_ref, float& lsum, const MlaFullStep& nx, int w, int lane) {
   const float cl = p.c_log2;
   f32x16 s = {};
   {
     u32x4 kf[WideCfg::SRING];
-    wide_s_pipe<0>(kf, s, qf, st + k_lat, st + k_rope);
+    wide_s_pipe<0, LOADS>(kf, s, qf, st + k_lat, st + k_rope, nx, w, lane);
   }
   u32x2 va[WideCfg::PVAHEAD + 1][2];
   const LDS_AS char* vp = st + v_off;
@@ -315,13 +324,28 @@ __global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaParams p) {
   for (int i = 0; i < nsteps; ++i) {
     mla_wait_loads<MlaCfg::LOADS_PER_WAVE>(nsteps - 1 - i);
     __syncthreads();  // step i visible to all; stage (i + 3) % 4 = (i - 1) % 4 read by all
-    if (i + 3 < nsteps) {
-      mla_issue(p, ri, it.k0 + 32 * (i + 3), pgA, pgB, w, lane, lds + ((i + 3) & 3) * MlaCfg::STAGE);
-      pgA = mla_page(p, ri, it.k0 + 32 * (i + 4));
-      pgB = mla_page(p, ri, it.k0 + 32 * (i + 4) + 16);
-    }
     const int b = it.k0 + 32 * i;
-    if (b < lim) wide_step(p, lds + (i & 3) * MlaCfg::STAGE, b, lim, h2, k_lat, k_rope, v_off, qf, m_ref, lsum);
+    const int b3 = b + 96;  // step i + 3, loaded during this step
+    const bool compute = b < lim;
+    // a full step i + 3 is loaded between this step's score products; a
+    // partial one, or any step when this one computes nothing, at once
+    const bool spread = compute && i + 3 < nsteps && b3 + 32 <= ri.kv;
+    MlaFullStep nx{};
+    if (spread) {
+      nx = mla_full_step(p, b3, pgA, pgB, lds + ((i + 3) & 3) * MlaCfg::STAGE);
+    } else if (i + 3 < nsteps) {
+      mla_issue(p, ri, b3, pgA, pgB, w, lane, lds + ((i + 3) & 3) * MlaCfg::STAGE);
+    }
+    if (i + 3 < nsteps) {
+      pgA = mla_page(p, ri, b3 + 32);
+      pgB = mla_page(p, ri, b3 + 48);
+    }
+    if (spread)
+      wide_step<true>(p, lds + (i & 3) * MlaCfg::STAGE, b, lim, h2, k_lat, k_rope, v_off, qf, m_ref, lsum, nx, w,
+                      lane);
+    else if (compute)
+      wide_step<false>(p, lds + (i & 3) * MlaCfg::STAGE, b, lim, h2, k_lat, k_rope, v_off, qf, m_ref, lsum, nx, w,
+                       lane);
   }
 
   acc_settle();
