@@ -595,7 +595,12 @@ __device__ __forceinline__ float prefill_exp(const f32x16 (&s)[2], float cl, flo
   return t[0] + t[1];
 }
 
-template <int D, bool MASK>
+// FIRST: the wavefront's first key tile (tile 0; m_ref = -inf, O and the
+// sums still zero).  The speculative pass would find every weight infinite
+// and be redone, so the row maximum is taken at once: the same values as the
+// general path's rescale branch (alpha = 0 there), one pass of exponentials.
+// Every row sees key 0, so the maximum is finite.
+template <int D, bool MASK, bool FIRST = false>
 __device__ __forceinline__ void prefill_softmax(const AttnParams& p, f32x16 (&s)[2], int kbase, int lim,
                                                 PrefillLanes ln, float& m_ref, float& lsum,
                                                 f32x16 (&oacc)[D / 32], uint32_t (&pk)[2][8]) {
@@ -607,6 +612,16 @@ __device__ __forceinline__ void prefill_softmax(const AttnParams& p, f32x16 (&s)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (kbase + 32 * kb + 8 * (r >> 2) + 4 * ln.h2 + (r & 3) >= lim) s[kb][r] = -INFINITY;
+  }
+  if constexpr (FIRST) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    m_ref = max_x32(mx);
+    lsum = prefill_exp<D>(s, cl, m_ref * cl, pk);
+    return;
   }
   float ts = prefill_exp<D>(s, cl, m_ref * cl, pk);
   // Some P of the tile reached 2^64, or is inf / NaN (the first tile, with
@@ -853,7 +868,7 @@ struct Prefill4Loop {
   int pk, pv;  // page ids of K(t + 2) and V(t + 1) for the loads of iteration t
 };
 
-template <int D, bool MASK, bool NEXT>
+template <int D, bool MASK, bool NEXT, bool FIRST = false>
 __device__ __forceinline__ void prefill_iter4(const AttnParams& p, const ReqInfo& ri, const PrefillItem& it,
                                               int t, int w, int lane, int wnt, int lim, PrefillLanes ln,
                                               const u32x4 (&qf)[D / 16], LDS_AS char* kbuf, LDS_AS char* vbuf,
@@ -876,7 +891,7 @@ __device__ __forceinline__ void prefill_iter4(const AttnParams& p, const ReqInfo
   if (t < wnt) {
     if (NEXT) prefill_scores<D>(kbuf + ((t + 1) & 1) * C::TILE_BYTES, ln, qf, s_next);
     uint32_t pk[2][8];
-    prefill_softmax<D, MASK>(p, s_cur, t * 64, lim, ln, m_ref, lsum, oacc, pk);
+    prefill_softmax<D, MASK, FIRST>(p, s_cur, t * 64, lim, ln, m_ref, lsum, oacc, pk);
     prefill_pv<D>(vbuf + (t & 1) * C::TILE_BYTES, ln, pk, oacc);
   }
 }
@@ -954,6 +969,23 @@ __device__ void prefill_tile4(const AttnParams& p, const PrefillItem& it, const 
 #define PD_PREFILL4_ITER(MASK, NEXT, T, CUR, NXT)                                                            \
   prefill_iter4<D, MASK, NEXT>(p, ri, it, T, w, lane, wnt, lim, ln, qf, kbuf, vbuf, L, CUR, NXT, m_ref, lsum, \
                                oacc)
+  // key tile 0 (with a next tile) on its own: its softmax takes the row
+  // maximum at once.  (Short prompts have few key tiles, so the general
+  // path's second pass over their first tile is a visible share of the
+  // work: 8 x 512 prompts 0.0609-0.0614 against 0.0620-0.0627 ms, same
+  // box.  The 8-wavefront kernel keeps the general path: there it measured
+  // 1 % slower on the long mixed launch.)
+  if (last > 0) {
+    if (n1 > 0)
+      prefill_iter4<D, false, true, true>(p, ri, it, 0, w, lane, wnt, lim, ln, qf, kbuf, vbuf, L, sa, sb, m_ref,
+                                          lsum, oacc);
+    else
+      prefill_iter4<D, true, true, true>(p, ri, it, 0, w, lane, wnt, lim, ln, qf, kbuf, vbuf, L, sa, sb, m_ref,
+                                         lsum, oacc);
+    kt = 1;
+    sa[0] = sb[0];
+    sa[1] = sb[1];
+  }
   for (; kt + 1 < n1; kt += 2) {
     PD_PREFILL4_ITER(false, true, kt, sa, sb);
     PD_PREFILL4_ITER(false, true, kt + 1, sb, sa);
