@@ -920,7 +920,9 @@ pd_status xfer_common(const pd_attn_desc* desc, const void* pool, const void* bu
     return fail(PD_ERR_WORKSPACE, "scratch smaller than 4 * n bytes");
   if ((s = check_ids(num_pool_pages, ids, n)) != PD_OK) return s;
   hipStream_t st = (hipStream_t)stream;
-  if ((s = staged_upload(scratch, ids, sizeof(int32_t) * (size_t)n, st)) != PD_OK) return s;
+  // short id lists travel in the kernel arguments; longer ones are staged
+  const bool inline_ids = n <= pdk::kXferInlineIds;
+  if (!inline_ids && (s = staged_upload(scratch, ids, sizeof(int32_t) * (size_t)n, st)) != PD_OK) return s;
   pdk::XferParams p{};
   p.buf = (char*)buf;
   p.pool0 = (void*)pool;
@@ -932,7 +934,7 @@ pd_status xfer_common(const pd_attn_desc* desc, const void* pool, const void* bu
   p.n = n;
   p.L = 1;
   p.to_buffer = to_buffer ? 1 : 0;
-  hipError_t e = pdk::launch_xfer(p, st);
+  hipError_t e = pdk::launch_xfer(p, inline_ids ? ids : nullptr, st);
   if (e != hipSuccess) return hip_fail(e, to_buffer ? "pack launch" : "unpack launch");
   return PD_OK;
 }
@@ -988,7 +990,7 @@ pd_status xfer_layers(pd_xfer_t x, void* d_ws, const void* d_buf, size_t buf_byt
   p.n = x->n;
   p.L = x->L;
   p.to_buffer = to_buffer ? 1 : 0;
-  hipError_t e = pdk::launch_xfer(p, (hipStream_t)stream);
+  hipError_t e = pdk::launch_xfer(p, nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, to_buffer ? "layer pack launch" : "layer unpack launch");
   return PD_OK;
 }
@@ -1414,7 +1416,8 @@ pd_status mla_xfer(const pd_mla_desc* desc, const void* pool, const void* buf, i
   if (scratch_bytes < sizeof(int32_t) * (size_t)n) return fail(PD_ERR_WORKSPACE, "scratch smaller than 4 * n bytes");
   if ((s = check_ids(num_pool_pages, ids, n)) != PD_OK) return s;
   hipStream_t st = (hipStream_t)stream;
-  if ((s = staged_upload(scratch, ids, sizeof(int32_t) * (size_t)n, st)) != PD_OK) return s;
+  const bool inline_ids = n <= pdk::kXferInlineIds;
+  if (!inline_ids && (s = staged_upload(scratch, ids, sizeof(int32_t) * (size_t)n, st)) != PD_OK) return s;
   pdk::XferParams p{};
   p.buf = (char*)buf;
   p.pool0 = (void*)pool;
@@ -1426,7 +1429,7 @@ pd_status mla_xfer(const pd_mla_desc* desc, const void* pool, const void* buf, i
   p.n = n;
   p.L = 1;
   p.to_buffer = to_buffer ? 1 : 0;
-  hipError_t e = pdk::launch_xfer(p, st);
+  hipError_t e = pdk::launch_xfer(p, inline_ids ? ids : nullptr, st);
   if (e != hipSuccess) return hip_fail(e, to_buffer ? "MLA pack launch" : "MLA unpack launch");
   return PD_OK;
 }

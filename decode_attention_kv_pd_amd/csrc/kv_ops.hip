@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "pd_internal.hpp"
 
 namespace pdk {
@@ -78,36 +80,101 @@ __global__ __launch_bounds__(kBlockThreads) void append_kernel(AppendParams p) {
 
 // ------------------------------------------------------------------------
 // Page transfers (pack / unpack, whole pages or a range of KV heads, one or
-// several layers).  Block (page i, 16 KiB slab y, layer l); grid order makes
-// the blocks of layer 0 dispatch first.  The slice of page p moved for
-// layer l is its K part then its V part, each seg_bytes long at seg_off in
-// its half (HND: a head range of a half is one contiguous run); in the
-// buffer it sits at ((l * n + i) * 2 + half) * seg_bytes.
-// Without a progress array the stores carry the non-temporal hint (each
-// byte is written once; measured on MI355X: pack 4.9 vs 4.6 TB/s, unpack 4.8
-// vs 4.2 TB/s, read + written).
-// With a progress array the copies are written through to memory (stores
-// coherent at system scope, so no L2 write-back is needed to publish them),
-// each block counts itself done once its stores are acknowledged, and the
-// last block of layer l to finish resets that layer's block counter (so the
-// next call starts from zero without a memset) and adds one to progress[l]
-// with a system-scope release store.
+// several layers).  The slice of page p moved for layer l is its K part then
+// its V part, each seg_bytes long at seg_off in its half (HND: a head range
+// of a half is one contiguous run); in the buffer it sits at ((l * n + i) *
+// 2 + half) * seg_bytes.  Items of work are (page i, 64 KiB slab y, layer
+// l): 16 chunks of 16 B per thread, all loads of a slab before its stores.
 // ------------------------------------------------------------------------
-// 16 chunks of 16 B per thread: a block moves a 64 KiB slab.  Measured on
-// MI355X (512 pages of 256 KiB, 8 layers): the write-through copies with
-// layer progress run at 5.1 TB/s read + written against 2.7 TB/s with 16 KiB
-// slabs (each block waits for its stores to be acknowledged before it
-// retires); plain pack / unpack stay at 4.7-4.8 TB/s.  (A release fence per
-// block after plain stores, instead of write-through, ran at 0.24 TB/s: the
-// L2 write-back it implies is per block.)
 constexpr int kPackChunksPerThread = 16;
+constexpr int64_t kSlabChunks = (int64_t)kBlockThreads * kPackChunksPerThread;
+
+// Plain single-layer transfers: a grid of at most kXferBlocks blocks strides
+// over the (page, slab) items; loads and stores carry the non-temporal hint
+// (every byte is read once and written once).  The page ids come from the
+// kernel arguments when they fit there (no upload before the launch) or from
+// device memory.  Measured on MI355X (512 pages of 256 KiB out of a
+// 4096-page pool, after a 1 GiB flush): pack 50 vs 54-55 us with one block
+// per (page, slab), unpack 53 vs 55 us; the ids in the arguments save the
+// 5-10 us that their upload added in front of every call.
+constexpr int kXferBlocks = 1024;
+struct XferInlineIds {
+  int32_t id[kXferInlineIds];
+};
+
+template <class Ids>
+__device__ __forceinline__ void xfer_plain(const XferParams& p, const Ids& ids) {
+  const int64_t segc = p.seg_bytes / 16;
+  const int64_t ny = (2 * segc + kSlabChunks - 1) / kSlabChunks;
+  const int64_t items = (int64_t)p.n * ny;
+  for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
+    const int i = (int)(w / ny);
+    const int64_t y = w - (int64_t)i * ny;
+    const int64_t page = ids(i);
+    char* buf = p.buf + (int64_t)i * 2 * p.seg_bytes;
+    char* pg = (char*)p.pool0 + page * p.page_bytes + p.seg_off;
+    const int64_t cs = y * kSlabChunks;  // first chunk of the slab
+    const int64_t c0 = cs + threadIdx.x;
+    u32x4 v[kPackChunksPerThread];
+    if (cs + kSlabChunks <= segc || (cs >= segc && cs + kSlabChunks <= 2 * segc)) {
+      // the whole slab lies in one half: one contiguous run on both sides
+      const int64_t pc = cs < segc ? cs * 16 : p.half_bytes + (cs - segc) * 16;
+      const char* src = (p.to_buffer ? pg + pc : buf + cs * 16) + 16 * threadIdx.x;
+      char* dst = (p.to_buffer ? buf + cs * 16 : pg + pc) + 16 * threadIdx.x;
+#pragma unroll
+      for (int k = 0; k < kPackChunksPerThread; ++k)
+        v[k] = __builtin_nontemporal_load((const u32x4*)(src + 16 * k * kBlockThreads));
+#pragma unroll
+      for (int k = 0; k < kPackChunksPerThread; ++k)
+        __builtin_nontemporal_store(v[k], (u32x4*)(dst + 16 * k * kBlockThreads));
+      continue;
+    }
+#pragma unroll
+    for (int k = 0; k < kPackChunksPerThread; ++k) {
+      const int64_t c = c0 + k * kBlockThreads;
+      if (c < 2 * segc) {
+        const int64_t pc = c < segc ? c * 16 : p.half_bytes + (c - segc) * 16;
+        v[k] = __builtin_nontemporal_load((const u32x4*)(p.to_buffer ? pg + pc : buf + c * 16));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPackChunksPerThread; ++k) {
+      const int64_t c = c0 + k * kBlockThreads;
+      if (c < 2 * segc) {
+        const int64_t pc = c < segc ? c * 16 : p.half_bytes + (c - segc) * 16;
+        __builtin_nontemporal_store(v[k], (u32x4*)(p.to_buffer ? buf + c * 16 : pg + pc));
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlockThreads) void xfer_plain_kernel(XferParams p) {
+  xfer_plain(p, [&](int i) { return p.page_ids[i]; });
+}
+__global__ __launch_bounds__(kBlockThreads) void xfer_inline_kernel(XferParams p, XferInlineIds ids) {
+  xfer_plain(p, [&](int i) { return ids.id[i]; });
+}
+
+// Multi-layer transfers with per-layer completion: block (page i, slab y,
+// layer l); grid order makes the blocks of layer 0 dispatch first.  The
+// copies are written through to memory (stores coherent at system scope, so
+// no L2 write-back is needed to publish them), each block counts itself
+// done once its stores are acknowledged, and the last block of layer l to
+// finish resets that layer's block counter (so the next call starts from
+// zero without a memset) and, with a progress array, adds one to
+// progress[l] with a system-scope release store.
+// Measured on MI355X (512 pages of 256 KiB, 8 layers): 5.1 TB/s read +
+// written with 64 KiB slabs against 2.7 TB/s with 16 KiB slabs (each block
+// waits for its stores to be acknowledged before it retires).  (A release
+// fence per block after plain stores, instead of write-through, ran at 0.24
+// TB/s: the L2 write-back it implies is per block.)
 
 // 16-byte vector store written through to memory (coherent at system scope).
 __device__ __forceinline__ void store16_sys(char* p, u32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
 }
 
-__global__ __launch_bounds__(kBlockThreads) void xfer_kernel(XferParams p) {
+__global__ __launch_bounds__(kBlockThreads) void xfer_layers_kernel(XferParams p) {
   const int i = blockIdx.x;
   const int l = blockIdx.z;
   const int64_t page = p.page_ids[i];
@@ -115,7 +182,7 @@ __global__ __launch_bounds__(kBlockThreads) void xfer_kernel(XferParams p) {
   const int64_t segc = p.seg_bytes / 16;
   char* buf = p.buf + ((int64_t)l * p.n + i) * 2 * p.seg_bytes;
   char* pg = pool + page * p.page_bytes + p.seg_off;
-  const int64_t c0 = (int64_t)blockIdx.y * kBlockThreads * kPackChunksPerThread + threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.y * kSlabChunks + threadIdx.x;
   u32x4 v[kPackChunksPerThread];
 #pragma unroll
   for (int k = 0; k < kPackChunksPerThread; ++k) {
@@ -125,36 +192,25 @@ __global__ __launch_bounds__(kBlockThreads) void xfer_kernel(XferParams p) {
       v[k] = *(const u32x4*)(p.to_buffer ? pg + pc : buf + c * 16);
     }
   }
-  if (!p.done) {
 #pragma unroll
-    for (int k = 0; k < kPackChunksPerThread; ++k) {
-      const int64_t c = c0 + k * kBlockThreads;
-      if (c < 2 * segc) {
-        const int64_t pc = c < segc ? c * 16 : p.half_bytes + (c - segc) * 16;
-        __builtin_nontemporal_store(v[k], (u32x4*)(p.to_buffer ? buf + c * 16 : pg + pc));
-      }
+  for (int k = 0; k < kPackChunksPerThread; ++k) {
+    const int64_t c = c0 + k * kBlockThreads;
+    if (c < 2 * segc) {
+      const int64_t pc = c < segc ? c * 16 : p.half_bytes + (c - segc) * 16;
+      store16_sys(p.to_buffer ? buf + c * 16 : pg + pc, v[k]);
     }
-  } else {
-#pragma unroll
-    for (int k = 0; k < kPackChunksPerThread; ++k) {
-      const int64_t c = c0 + k * kBlockThreads;
-      if (c < 2 * segc) {
-        const int64_t pc = c < segc ? c * 16 : p.half_bytes + (c - segc) * 16;
-        store16_sys(p.to_buffer ? buf + c * 16 : pg + pc, v[k]);
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have reached memory
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t blocks = gridDim.x * gridDim.y;
-      const uint32_t prev = __hip_atomic_fetch_add(p.done + l, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == blocks - 1) {
-        __hip_atomic_store(p.done + l, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (p.progress) {
-          __threadfence_system();
-          const uint32_t n = __hip_atomic_load(p.progress + l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-          __hip_atomic_store(p.progress + l, n + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-        }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have reached memory
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t blocks = gridDim.x * gridDim.y;
+    const uint32_t prev = __hip_atomic_fetch_add(p.done + l, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == blocks - 1) {
+      __hip_atomic_store(p.done + l, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (p.progress) {
+        __threadfence_system();
+        const uint32_t n = __hip_atomic_load(p.progress + l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(p.progress + l, n + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
   }
@@ -169,12 +225,22 @@ hipError_t launch_append(const AppendParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_xfer(const XferParams& p, hipStream_t s) {
+hipError_t launch_xfer(const XferParams& p, const int32_t* host_ids, hipStream_t s) {
   if (p.n == 0 || p.L == 0) return hipSuccess;
-  const int64_t chunks = 2 * p.seg_bytes / 16;
-  const int64_t per_block = (int64_t)kBlockThreads * kPackChunksPerThread;
-  const unsigned ny = (unsigned)((chunks + per_block - 1) / per_block);
-  hipLaunchKernelGGL(xfer_kernel, dim3(p.n, ny, p.L), dim3(kBlockThreads), 0, s, p);
+  if (p.done) {
+    const unsigned ny = (unsigned)((2 * p.seg_bytes / 16 + kSlabChunks - 1) / kSlabChunks);
+    hipLaunchKernelGGL(xfer_layers_kernel, dim3(p.n, ny, p.L), dim3(kBlockThreads), 0, s, p);
+    return hipGetLastError();
+  }
+  const int64_t items = (int64_t)p.n * ((2 * p.seg_bytes / 16 + kSlabChunks - 1) / kSlabChunks);
+  const unsigned blocks = (unsigned)std::min<int64_t>(items, kXferBlocks);
+  if (host_ids && p.n <= kXferInlineIds) {
+    XferInlineIds ids;
+    std::copy(host_ids, host_ids + p.n, ids.id);
+    hipLaunchKernelGGL(xfer_inline_kernel, dim3(blocks), dim3(kBlockThreads), 0, s, p, ids);
+  } else {
+    hipLaunchKernelGGL(xfer_plain_kernel, dim3(blocks), dim3(kBlockThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -186,6 +186,11 @@ hipError_t launch_mla_append(const MlaParams& p, void* pool, const void* rows_ne
 hipError_t launch_attention(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_merge(const AttnParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
-hipError_t launch_xfer(const XferParams& p, hipStream_t s);
+// Single-layer transfers of at most kXferInlineIds pages take their page ids
+// from host_ids in the kernel arguments (p.page_ids unused); otherwise
+// p.page_ids is a device array.  Multi-layer transfers (p.done set) always
+// read p.page_ids.
+constexpr int kXferInlineIds = 896;
+hipError_t launch_xfer(const XferParams& p, const int32_t* host_ids, hipStream_t s);
 
 }  // namespace pdk

@@ -275,9 +275,12 @@ size_t pd_kv_pack_bytes(const pd_attn_desc* desc, int32_t n_pages);
  * request's whole page list at once is the request-level transfer
  * granularity of the kwkr.cn survey, section 5.4.
  *   page_ids   HOST array of n page ids in [0, num_pool_pages), no repeats;
- *              copied to d_scratch on `stream` before the call returns
+ *              up to 896 ids travel in the kernel arguments, longer lists
+ *              are copied to d_scratch on `stream`; either way the array
+ *              may be reused once the call returns
  *   d_buf      device buffer of buf_bytes >= pd_kv_pack_bytes(desc, n)
- *   d_scratch  device scratch of scratch_bytes >= 4 * n
+ *   d_scratch  device scratch of scratch_bytes >= 4 * n (written only when
+ *              n > 896)
  * Errors: PD_ERR_INVALID_ARG, PD_ERR_OUT_OF_RANGE, PD_ERR_WORKSPACE,
  * PD_ERR_UNSUPPORTED, PD_ERR_HIP.  n == 0 is a no-op. */
 pd_status pd_kv_pack(const pd_attn_desc* desc, const void* kv_pool,
@@ -313,7 +316,8 @@ size_t pd_kv_pack_heads_bytes(const pd_attn_desc* desc, int32_t n_pages,
  * contiguous buffer [n][2][h1 - h0][page_size][head_dim] (K slice then V
  * slice of each page; bit-exact).  h0 = 0, h1 = num_kv_heads is pd_kv_pack.
  *   page_ids   HOST array of n page ids in [0, num_pool_pages), no repeats;
- *              staged through pinned memory to d_scratch on `stream`
+ *              passed as in pd_kv_pack (kernel arguments up to 896 ids,
+ *              else staged through pinned memory to d_scratch on `stream`)
  *   d_buf      device buffer of buf_bytes >= pd_kv_pack_heads_bytes(...)
  *   d_scratch  device scratch of scratch_bytes >= 4 * n
  * Errors: PD_ERR_INVALID_ARG (head range not within [0, num_kv_heads) or
@@ -509,8 +513,8 @@ pd_status pd_mla_attention_run(pd_plan_t plan, void* d_ws, const void* q,
 
 /* Copy whole latent pages (list order) into one contiguous buffer
  * [n][page bytes], and back into (other) page ids.  Every rank holds the
- * same latent pages, so a page travels whole from any one rank (post,
- * section "Sharded KV Cache Transfers").  Arguments and errors as
+ * same latent pages (post, section "DeepSeek-R1"), so a page travels whole
+ * from any one rank.  Arguments and errors as
  * pd_kv_pack / pd_kv_unpack (buf_bytes >= n * pd_mla_page_bytes). */
 pd_status pd_mla_kv_pack(const pd_mla_desc* desc, const void* kv_pool,
                          int32_t num_pool_pages, const int32_t* page_ids,
