@@ -96,3 +96,31 @@ def test_attention_reads_no_nan_from_poisoned_slots():
     assert torch.equal(before.view(torch.int16), run.pool.view(torch.int16))
     n = int(b.qo_indptr[-1])
     assert torch.isfinite(run.out[:n]).all() and torch.isfinite(run.lse[:n]).all()
+
+
+@pytest.mark.parametrize("n", [896, 897, 1500])
+def test_pack_unpack_long_id_lists(n):
+    """Lists of up to 896 page ids travel in the kernel arguments, longer
+    ones are staged to the scratch: both paths bit-exact (the scratch starts
+    as garbage, so ids read from the wrong place would show)."""
+    b = batch("mixed", None)
+    print(f"pack {n} pages of the mixed batch", flush=True)
+    m = pd()
+    run = DeviceRun(b)
+    run.append()
+    assert len(b.page_indices) >= n
+    ids = np.random.default_rng(n).permutation(b.page_indices)[:n].astype(np.int32)
+    buf = torch.empty(m.pd_kv_pack_bytes(run.desc, n), dtype=torch.uint8, device="cuda")
+    scratch = torch.full((4 * n,), 0xFF, dtype=torch.uint8, device="cuda")
+    m.pd_kv_pack(run.desc, run.pool, b.num_pool_pages, ids, buf, scratch)
+    torch.cuda.synchronize()
+    pool_now = host_array(run.pool, b.np_dtype)
+    ref = OP.kv_pack(pool_now, ids)
+    assert buf.cpu().numpy().tobytes() == ref.tobytes()
+    dst = np.random.default_rng(n + 1).permutation(b.num_pool_pages)[:n].astype(np.int32)
+    fresh = np.full_like(pool_now, 0x7FC0)
+    pool2 = dev_array(fresh)
+    scratch.fill_(0xFF)
+    m.pd_kv_unpack(run.desc, pool2, b.num_pool_pages, dst, buf, scratch)
+    torch.cuda.synchronize()
+    assert host_array(pool2, b.np_dtype).tobytes() == OP.kv_unpack(fresh.copy(), dst, ref).tobytes()
