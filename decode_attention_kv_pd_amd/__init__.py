@@ -44,7 +44,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpd_attn.so")
+# the in-tree library; PD_ATTN_LIB names another build of it (for instance one
+# whose host code carries sanitizers, see build.py)
+LIB_PATH = os.environ.get("PD_ATTN_LIB") or os.path.join(_HERE, "libpd_attn.so")
 
 PD_F32 = 0
 PD_BF16 = 1

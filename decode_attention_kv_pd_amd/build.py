@@ -40,12 +40,21 @@ COMMON = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
 
 
-def compile_command(src: str, obj: str):
-    return [hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
+# Host-code sanitizers (AddressSanitizer + UndefinedBehaviorSanitizer) for the
+# planner and the C ABI: applied to the host pass only (-Xarch_host), never to
+# GPU code.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined"]
 
 
-def link_command(objs, out: str):
-    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
+def compile_command(src: str, obj: str, sanitize: bool = False):
+    extra = HOST_SANITIZE if sanitize and src.endswith(".cpp") else []
+    return [hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
+
+
+def link_command(objs, out: str, sanitize: bool = False):
+    extra = ["-fsanitize=address,undefined", "-shared-libasan"] if sanitize else []
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", out]
 
 
 def _errors(res) -> str:
@@ -53,34 +62,37 @@ def _errors(res) -> str:
     return "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
+    """Compile every source and link the library at `out`.  `sanitize`
+    instruments the host code (api.cpp) with ASan and UBSan; such a library
+    is loaded with the sanitizer runtime preloaded (see __main__ below)."""
+    tmp = out + ".tmp"
     with tempfile.TemporaryDirectory(prefix="pd_attn_build_") as d:
         objs, procs = [], []
         for src in SOURCES:
             obj = os.path.join(d, os.path.basename(src) + ".o")
-            cmd = compile_command(src, obj)
+            cmd = compile_command(src, obj, sanitize)
             if verbose:
                 print(" ".join(cmd), flush=True)
             objs.append(obj)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
         failed = []
         for src, pr in procs:
-            out, err = pr.communicate()
-            res = subprocess.CompletedProcess(pr.args, pr.returncode, out, err)
+            o, e = pr.communicate()
+            res = subprocess.CompletedProcess(pr.args, pr.returncode, o, e)
             if res.returncode != 0:
                 failed.append(f"{os.path.basename(src)}: hipcc failed ({res.returncode}):\n{_errors(res)}")
             elif verbose and _errors(res).strip():
                 print(_errors(res), file=sys.stderr)
         if failed:
             raise RuntimeError("\n".join(failed))
-        cmd = link_command(objs, tmp)
+        cmd = link_command(objs, tmp, sanitize)
         if verbose:
             print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"link failed ({res.returncode}):\n{_errors(res)}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     # static checks of the 32-row MLA kernel's generated code (isa_check.py)
     spec = importlib.util.spec_from_file_location("_pd_isa_check", os.path.join(HERE, "isa_check.py"))
     chk = importlib.util.module_from_spec(spec)
@@ -88,8 +100,19 @@ def build(verbose: bool = False) -> str:
     chk.run(hipcc(), COMMON)
     if verbose:
         print("isa check: mla_wide_kernel ok", flush=True)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    # python decode_attention_kv_pd_amd/build.py                  -> the library in place
+    # python decode_attention_kv_pd_amd/build.py --host-sanitize DIR
+    #   -> DIR/libpd_attn.so with ASan/UBSan host code; run the host tests
+    #      against it with the runtime preloaded, e.g.
+    #      LD_PRELOAD=$(hipcc --print-file-name=libclang_rt.asan-x86_64.so)
+    #      ASAN_OPTIONS=detect_leaks=0 PD_ATTN_LIB=DIR/libpd_attn.so
+    #      python -m pytest tests/test_host_abi.py tests/test_host_mla.py
+    if len(sys.argv) == 3 and sys.argv[1] == "--host-sanitize":
+        os.makedirs(sys.argv[2], exist_ok=True)
+        print(build(verbose=True, out=os.path.join(sys.argv[2], "libpd_attn.so"), sanitize=True))
+    else:
+        print(build(verbose=True))
