@@ -20,7 +20,7 @@ import pytest
 import torch
 
 from oracle import attention as OA
-from tests.harness import DeviceRun, oracle_outputs, report, tolerance
+from tests.harness import DeviceRun, oracle_outputs, pd, report, tolerance
 from workloads import bf16_bits_to_f32, f32_to_bf16_bits, make_batch
 
 pytestmark = pytest.mark.gpu
@@ -310,3 +310,53 @@ def test_interference_sweep_batches(L):
         out_p, _ = DeviceRun(part).step()
         rows = np.repeat(sel, qo)
         assert np.abs(out_p - out_m[rows]).max() <= 2 * tolerance(b)
+
+
+def test_step_in_graph_replays():
+    """The whole step (append, the attention launch and its merge, pack and
+    unpack of a request's pages) captured once in a HIP graph and replayed
+    three times, with the pool restored and the outputs poisoned eagerly in
+    between: every replay equals the eager step bit for bit (the step holds
+    kernel launches only, with the page ids in the transfer's arguments, so
+    it can be captured; post, section "KV Messenger")."""
+    b = batch("mixed")
+    m = pd()
+    run = DeviceRun(b)
+    pool0 = run.pool.clone()
+    ids = b.request_pages(0)
+    dst = np.random.default_rng(3).permutation(b.spare_pages)[:len(ids)].astype(np.int32)
+    assert 0 < len(ids) <= len(dst)
+    nbytes = m.pd_kv_pack_bytes(run.desc, len(ids))
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(4 * len(ids), dtype=torch.uint8, device="cuda")
+
+    def step():
+        run.append()
+        run.attention()
+        m.pd_kv_pack(run.desc, run.pool, b.num_pool_pages, ids, buf, scratch)
+        m.pd_kv_unpack(run.desc, run.pool, b.num_pool_pages, dst, buf, scratch)
+
+    step()  # eager reference (also loads every kernel before the capture)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (run.out, run.lse, buf, run.pool)]
+    n = int(b.qo_indptr[-1])
+    O, _ = oracle_outputs(b)
+    assert report("graph eager", run.out[:n].cpu().numpy(), O) <= tolerance(b)
+    g = torch.cuda.CUDAGraph()
+    run.pool.copy_(pool0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        run.pool.copy_(pool0)           # eager work between replays
+        run.out.fill_(float("nan"))
+        run.lse.fill_(float("nan"))
+        buf.fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = [torch.equal(a.view(torch.uint8), r.view(torch.uint8))
+                for a, r in zip((run.out, run.lse, buf, run.pool), ref)]
+        print(f"replay {rep}: out/lse/buf/pool bitwise equal {same}", flush=True)
+        assert all(same)
