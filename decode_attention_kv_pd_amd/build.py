@@ -62,6 +62,26 @@ def _errors(res) -> str:
     return "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
 
 
+def build_c_step(verbose: bool = False) -> str:
+    """tests/c_step: the C program of tests/test_gpu_c_abi.py, which drives a
+    step through the C ABI with the HIP runtime alone (no PyTorch); built
+    with the C compiler against include/pd_attn.h and the library."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    src = os.path.join(ROOT, "tests", "c_step.c")
+    exe = os.path.join(ROOT, "tests", "c_step")
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(rocm, "include"), src, "-o", exe, "-L", HERE, "-lpd_attn", "-L", os.path.join(rocm, "lib"),
+           "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../decode_attention_kv_pd_amd", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"c_step build failed ({res.returncode}):\n{res.stderr}")
+    return exe
+
+
 def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
     """Compile every source and link the library at `out`.  `sanitize`
     instruments the host code (api.cpp) with ASan and UBSan; such a library
@@ -93,6 +113,8 @@ def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
         if res.returncode != 0:
             raise RuntimeError(f"link failed ({res.returncode}):\n{_errors(res)}")
     os.replace(tmp, out)
+    if out == LIB:
+        build_c_step(verbose)
     # static checks of the 32-row MLA kernel's generated code (isa_check.py)
     spec = importlib.util.spec_from_file_location("_pd_isa_check", os.path.join(HERE, "isa_check.py"))
     chk = importlib.util.module_from_spec(spec)
